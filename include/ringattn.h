@@ -1,0 +1,175 @@
+/*
+ * ringattn.h - C ABI of the gfx950 (MI355X) library for one device's share of
+ * exact ring attention.
+ *
+ * What is computed.  A device holds a local query chunk and receives the key /
+ * value blocks of the sequence one at a time in ring order ("Ring Attention:
+ * Train 1M Tokens on 8GB GPUs in 2026", section "Ring Attention: Partition
+ * Sequence Length, Not Batch").  Each block is attended blockwise while the
+ * next one is in flight ("Ring Attention with Blockwise Transformers for
+ * Near-Infinite Context", Abstract), and the partial results are merged
+ * through the state triple named in the "Gotchas and Failure Modes" section of
+ * the tildalice page: running max m, running sum l and unnormalised output
+ * acc.  After the last block the output is softmax(Q K^T * scale) V over every
+ * visible key (the attention equation of the section "Why Standard Attention
+ * Explodes Past 100K Tokens", scale = 1/sqrt(d)) and LSE is its natural-log
+ * log-sum-exp.  The merge is the exact online-softmax rule (Milakov and
+ * Gimelshein, "Online normalizer calculation for softmax", cited in the arXiv
+ * record's reference list), so the result does not depend on block order up
+ * to rounding.
+ *
+ * Tensors and layout.
+ *   Q, every K/V block and O are [B, S, H, D] with element strides
+ *   (stride_b, stride_s, stride_h) and unit stride along D.  Query row r sits
+ *   at global position q_pos0 + r; key j of a block at that block's
+ *   kv_pos0 + j.  Causal masking: a key is visible iff its position <= the
+ *   query's position (diagonal included).
+ *   State: m, l  [B, H, Sq] fp32 contiguous; acc [B, H, Sq, D] fp32
+ *   contiguous; m is in natural-log score units (max of scale * q.k).
+ *   LSE [B, H, Sq] fp32 contiguous.  A row that has seen no visible key has
+ *   m = -inf, l = 0, acc = 0, and is finalized to O = 0, LSE = -inf.
+ *   The state triple is defined up to the choice of m: any (m, l, acc) with
+ *   l = sum exp(s - m) and acc = sum exp(s - m) v over the keys seen so far
+ *   is a valid state, and acc/l and m + ln l do not depend on that choice.
+ *
+ * An empty query chunk (q_len = 0) is valid: such a call checks the
+ * descriptor, then returns RA_OK without looking at any pointer (empty
+ * tensors may have NULL data) and enqueues nothing.
+ *
+ * Dtypes: (in, out) = (F32, F32), (BF16, BF16) or (BF16, F32).  BF16 inputs
+ * use bf16 matrix cores with fp32 accumulation; F32 inputs are computed in
+ * fp32 throughout.
+ *
+ * Ownership and synchronisation.  The caller owns all memory: inputs,
+ * outputs, the state workspace and the staging slots.  The library allocates
+ * no device memory.  Every call validates its arguments completely before it
+ * enqueues anything; on error it returns a non-zero status, enqueues nothing
+ * and leaves all buffers untouched, and ringattn_last_error() holds a
+ * message for the calling thread.  On success the work is enqueued on the
+ * given stream(s) and the call returns without synchronising; results are
+ * valid once the compute stream has finished.  Faults inside kernels surface
+ * at the caller's next synchronisation.  Nothing throws or aborts across the
+ * ABI.  Calls that share buffers on overlapping streams race; calls on
+ * disjoint buffers may run concurrently.
+ */
+#ifndef RINGATTN_H
+#define RINGATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RINGATTN_ABI_VERSION 1
+
+typedef enum ra_status {
+  RA_OK = 0,
+  RA_E_NULL = 1,        /* a required pointer is NULL                           */
+  RA_E_SHAPE = 2,       /* negative / inconsistent sizes or strides             */
+  RA_E_DTYPE = 3,       /* unsupported (in, out) dtype pair                     */
+  RA_E_ALIGN = 4,       /* base pointer or row not 16-byte aligned              */
+  RA_E_UNSUPPORTED = 5, /* valid request outside what the kernels implement     */
+  RA_E_MEMTYPE = 6,     /* pointer is not the kind of memory the call needs     */
+  RA_E_HIP = 7          /* a HIP runtime call failed (message has the HIP text) */
+} ra_status;
+
+typedef enum ra_dtype { RA_F32 = 0, RA_BF16 = 1 } ra_dtype;
+
+/* ring_fwd path selection (ra_desc.flags). */
+#define RA_FLAG_PERBLOCK 1 /* force init_state + block_fwd per block + finalize */
+
+typedef struct ra_desc {
+  int32_t batch;       /* B >= 1                                              */
+  int32_t heads;       /* H >= 1 (key/value heads equal query heads)          */
+  int32_t head_dim;    /* D: 64 or 128                                        */
+  int32_t causal;      /* 1: key visible iff kv_pos <= q_pos; 0: all visible   */
+  int64_t q_len;       /* Sq >= 0: rows of the local query chunk              */
+  int64_t kv_len;      /* Ck >= 0: keys per KV block (all blocks equal)        */
+  int64_t q_pos0;      /* global position of query row 0 (q_idx * Sq)         */
+  float scale;         /* softmax temperature; <= 0 selects 1/sqrt(D)         */
+  int32_t in_dtype;    /* ra_dtype of Q, K, V                                 */
+  int32_t out_dtype;   /* ra_dtype of O                                       */
+  int32_t flags;       /* RA_FLAG_*                                           */
+  int64_t q_stride[3]; /* element strides of Q along (b, s, h)                */
+  int64_t kv_stride[3];/* element strides of every K and V block              */
+  int64_t o_stride[3]; /* element strides of O                                */
+} ra_desc;
+
+/* Block classes returned by ringattn_block_class. */
+#define RA_BLOCK_SKIP 0 /* causal and no key of the block is visible to any row */
+#define RA_BLOCK_FULL 1 /* every key visible to every row                       */
+#define RA_BLOCK_DIAG 2 /* some keys visible to some rows: masked per element   */
+
+/* Maximum number of device-resident blocks one fused launch carries; longer
+ * rings are processed in segments of this many blocks with the state kept in
+ * the caller's workspace between segments. */
+#define RA_FUSED_MAX_BLOCKS 64
+
+int ringattn_abi_version(void);
+const char* ringattn_status_str(int status);
+/* Detail of the last failing call on this thread ("" if none). */
+const char* ringattn_last_error(void);
+
+/* Ring schedule of the tildalice page, section "Ring Attention: Partition
+ * Sequence Length, Not Batch": at step s the device at ring index q_idx holds
+ * the block that started on device (q_idx - s) mod P.  Writes that block index
+ * for s = 0..P-1 into order[P] (host memory).  Host only. */
+ra_status ringattn_ring_order(int32_t q_idx, int32_t num_devices, int32_t* order);
+
+/* Causal class of the block starting at kv_pos0 with respect to the query
+ * chunk of desc (RA_BLOCK_*); non-causal descriptors give RA_BLOCK_FULL for a
+ * non-empty block.  Empty chunks or blocks give RA_BLOCK_SKIP.  Host only;
+ * returns -1 for a NULL desc. */
+int32_t ringattn_block_class(const ra_desc* desc, int64_t kv_pos0);
+
+/* Start a ring pass: m = -inf, l = 0, acc = 0 (device pointers, layouts above). */
+ra_status ringattn_init_state(const ra_desc* desc, float* m, float* l, float* acc, hipStream_t stream);
+
+/* Attend the query chunk q to one KV block (device pointers k, v whose keys
+ * sit at kv_pos0 + 0..kv_len-1) and fold the result into (m, l, acc) by the
+ * online-softmax rule.  A block with no key visible to any row enqueues
+ * nothing and returns RA_OK. */
+ra_status ringattn_block_fwd(const ra_desc* desc, const void* q, const void* k, const void* v, int64_t kv_pos0,
+                             float* m, float* l, float* acc, hipStream_t stream);
+
+/* End a ring pass: O = acc / l in out_dtype (0 where l = 0), LSE = m + ln l
+ * (-inf where l = 0). */
+ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l, const float* acc, void* o,
+                            float* lse, hipStream_t stream);
+
+/* Whole ring pass over num_blocks >= 0 blocks given in processing (ring) order:
+ * k_blocks[i], v_blocks[i] hold the keys at kv_pos0[i] + 0..kv_len-1.  The
+ * arrays k_blocks, v_blocks, kv_pos0 are host memory.  Equivalent to
+ * init_state, block_fwd for each block in array order, finalize; the fused
+ * path keeps the state on chip and may differ from the per-block path only by
+ * rounding.
+ *
+ * kv_on_host = 0: blocks are device memory.  Unless flags has
+ *   RA_FLAG_PERBLOCK, a fused kernel runs (m, l, acc may be NULL when
+ *   num_blocks <= RA_FUSED_MAX_BLOCKS; otherwise they are required).
+ * kv_on_host = 1: blocks are pinned host memory (hipHostMalloc'd or
+ *   registered), each block densely packed [B, Ck, H, D].  stage_k[0..1] and
+ *   stage_v[0..1] are four device slots of B*Ck*H*D elements each; block i is
+ *   copied into slot i%2 with hipMemcpyAsync on `copy` while the block before
+ *   it is computed on `compute`; per-slot events order the copy before the
+ *   kernel and the kernel before the slot's next copy.  m, l, acc are
+ *   required.  `copy` must differ from `compute`.  The host blocks must stay
+ *   alive and unchanged until the compute stream has finished.
+ * O and LSE are written on `compute`. */
+ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* const* k_blocks,
+                            const void* const* v_blocks, const int64_t* kv_pos0, int32_t num_blocks,
+                            int32_t kv_on_host, void* const* stage_k, void* const* stage_v, float* m, float* l,
+                            float* acc, void* o, float* lse, hipStream_t compute, hipStream_t copy);
+
+/* Measurement helper, not part of the attention path: a plain device-to-device
+ * copy kernel of `bytes` (multiple of 16, 16-byte aligned pointers), used to
+ * calibrate hardware byte counters and HBM bandwidth. */
+ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RINGATTN_H */

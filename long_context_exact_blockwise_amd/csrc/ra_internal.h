@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI host layer (ringattn_api.hip) and the
+// kernel translation units.  Not installed; not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+#include "../../include/ringattn.h"
+
+namespace ra {
+
+// Device-resident KV blocks handed to one fused launch, in processing order.
+// Passed by value as a kernel argument (fits the kernel-argument segment).
+struct BlockTable {
+  const void* k[RA_FUSED_MAX_BLOCKS];
+  const void* v[RA_FUSED_MAX_BLOCKS];
+  int64_t pos0[RA_FUSED_MAX_BLOCKS];
+};
+
+// How a launch starts and ends its rows' state.
+enum StateMode : int {
+  kInitFinalize = 0,  // start from m=-inf,l=0,acc=0; end by writing O and LSE
+  kInitStore = 1,     // start from the empty state; end by storing (m,l,acc)
+  kLoadStore = 2,     // load (m,l,acc); store it back
+  kLoadFinalize = 3,  // load (m,l,acc); end by writing O and LSE
+};
+
+struct AttnArgs {
+  const void* q;
+  void* o;
+  float* lse;
+  float* m;
+  float* l;
+  float* acc;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t kv_sb, kv_ss, kv_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t q_len, kv_len, q_pos0;
+  int32_t batch, heads, head_dim, causal, nblocks;
+  float scale;        // softmax temperature (natural-log units)
+  int32_t out_bf16;   // 1: O is bf16, 0: fp32
+};
+
+// Launchers: validate nothing (the API layer did), enqueue, return the launch
+// error (hipSuccess on success).
+hipError_t launch_attn_bf16(const AttnArgs& a, const BlockTable& t, int mode, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, const BlockTable& t, int mode, hipStream_t s);
+hipError_t launch_init_state(int64_t rows, int32_t d, float* m, float* l, float* acc, hipStream_t s);
+hipError_t launch_finalize(const AttnArgs& a, hipStream_t s);
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+
+}  // namespace ra

@@ -1,0 +1,420 @@
+// C-ABI host layer: argument validation, causal block classification, the
+// ring replay driver (fused, per-block, and host-streamed with copy/compute
+// overlap) and error reporting.  Every entry point validates completely
+// before it enqueues anything and never throws across the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "ra_internal.h"
+
+namespace {
+
+using ra::AttnArgs;
+using ra::BlockTable;
+
+thread_local std::string g_err;
+
+ra_status fail(ra_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ra_status hip_fail(hipError_t e, const char* what) {
+  return fail(RA_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+int esize(int32_t dt) { return dt == RA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Host-only checks of a descriptor (no HIP calls).
+ra_status check_desc(const ra_desc* d) {
+  if (!d) return fail(RA_E_NULL, "desc is NULL");
+  if (d->batch < 1 || d->heads < 1) return fail(RA_E_SHAPE, "batch (%d) and heads (%d) must be >= 1", d->batch, d->heads);
+  if (d->q_len < 0 || d->kv_len < 0)
+    return fail(RA_E_SHAPE, "q_len (%lld) and kv_len (%lld) must be >= 0", (long long)d->q_len, (long long)d->kv_len);
+  if (d->causal != 0 && d->causal != 1) return fail(RA_E_SHAPE, "causal must be 0 or 1 (got %d)", d->causal);
+  if (std::isnan(d->scale) || std::isinf(d->scale)) return fail(RA_E_SHAPE, "scale must be finite");
+  if ((d->flags & ~RA_FLAG_PERBLOCK) != 0) return fail(RA_E_UNSUPPORTED, "unknown flags 0x%x", d->flags);
+  const bool ok_dt = (d->in_dtype == RA_F32 && d->out_dtype == RA_F32) ||
+                     (d->in_dtype == RA_BF16 && (d->out_dtype == RA_BF16 || d->out_dtype == RA_F32));
+  if (!ok_dt) return fail(RA_E_DTYPE, "unsupported (in, out) dtype pair (%d, %d)", d->in_dtype, d->out_dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(RA_E_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", d->head_dim);
+  const int64_t* sts[3] = {d->q_stride, d->kv_stride, d->o_stride};
+  const char* names[3] = {"q_stride", "kv_stride", "o_stride"};
+  const int es[3] = {esize(d->in_dtype), esize(d->in_dtype), esize(d->out_dtype)};
+  for (int t = 0; t < 3; ++t) {
+    const int64_t dims[3] = {d->batch, t == 1 ? d->kv_len : d->q_len, d->heads};
+    for (int i = 0; i < 3; ++i) {
+      if (dims[i] > 1 && sts[t][i] <= 0)
+        return fail(RA_E_SHAPE, "%s[%d] = %lld must be positive", names[t], i, (long long)sts[t][i]);
+      if ((sts[t][i] * es[t]) % 16 != 0)
+        return fail(RA_E_ALIGN, "%s[%d] = %lld elements is not a multiple of 16 bytes", names[t], i,
+                    (long long)sts[t][i]);
+    }
+  }
+  // The kernels address one 64-key tile of a block with 32-bit byte offsets.
+  if (d->kv_stride[1] * esize(d->in_dtype) * 64 >= (int64_t)1 << 31)
+    return fail(RA_E_UNSUPPORTED, "kv_stride[1] too large (a 64-key tile must span < 2 GiB)");
+  return RA_OK;
+}
+
+ra_status need_ptr(const void* p, const char* name) {
+  if (!p) return fail(RA_E_NULL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(RA_E_ALIGN, "%s is not 16-byte aligned", name);
+  return RA_OK;
+}
+
+// Memory-kind checks (HIP calls).  want_host: pinned host memory; else device.
+ra_status check_mem(const void* p, bool want_host, const char* name) {
+  hipPointerAttribute_t attr;
+  std::memset(&attr, 0, sizeof attr);
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    if (e == hipErrorInvalidValue)
+      return fail(RA_E_MEMTYPE, "%s is not memory known to HIP (pageable host memory?)", name);
+    return hip_fail(e, "hipPointerGetAttributes");
+  }
+  const int t = (int)attr.type;
+  if (want_host) {
+    if (t != hipMemoryTypeHost) return fail(RA_E_MEMTYPE, "%s must be pinned host memory (type %d)", name, t);
+  } else {
+    if (t != hipMemoryTypeDevice && t != hipMemoryTypeManaged)
+      return fail(RA_E_MEMTYPE, "%s must be device memory (type %d)", name, t);
+  }
+  return RA_OK;
+}
+
+int32_t classify(const ra_desc* d, int64_t kv_pos0) {
+  if (d->q_len == 0 || d->kv_len == 0) return RA_BLOCK_SKIP;
+  if (!d->causal) return RA_BLOCK_FULL;
+  const int64_t q_first = d->q_pos0, q_last = d->q_pos0 + d->q_len - 1;
+  const int64_t k_first = kv_pos0, k_last = kv_pos0 + d->kv_len - 1;
+  if (k_first > q_last) return RA_BLOCK_SKIP;
+  if (k_last <= q_first) return RA_BLOCK_FULL;
+  return RA_BLOCK_DIAG;
+}
+
+AttnArgs make_args(const ra_desc* d, const void* q, void* o, float* lse, float* m, float* l, float* acc) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q;
+  a.o = o;
+  a.lse = lse;
+  a.m = m;
+  a.l = l;
+  a.acc = acc;
+  a.q_sb = d->q_stride[0];
+  a.q_ss = d->q_stride[1];
+  a.q_sh = d->q_stride[2];
+  a.kv_sb = d->kv_stride[0];
+  a.kv_ss = d->kv_stride[1];
+  a.kv_sh = d->kv_stride[2];
+  a.o_sb = d->o_stride[0];
+  a.o_ss = d->o_stride[1];
+  a.o_sh = d->o_stride[2];
+  a.q_len = d->q_len;
+  a.kv_len = d->kv_len;
+  a.q_pos0 = d->q_pos0;
+  a.batch = d->batch;
+  a.heads = d->heads;
+  a.head_dim = d->head_dim;
+  a.causal = d->causal;
+  a.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  a.out_bf16 = d->out_dtype == RA_BF16;
+  return a;
+}
+
+hipError_t launch_attn(const ra_desc* d, AttnArgs a, const BlockTable& t, int nblocks, int mode, hipStream_t s) {
+  a.nblocks = nblocks;
+  return d->in_dtype == RA_BF16 ? ra::launch_attn_bf16(a, t, mode, s) : ra::launch_attn_f32(a, t, mode, s);
+}
+
+ra_status check_state_ptrs(float* m, float* l, float* acc) {
+  ra_status st;
+  if ((st = need_ptr(m, "m")) != RA_OK) return st;
+  if ((st = need_ptr(l, "l")) != RA_OK) return st;
+  if ((st = need_ptr(acc, "acc")) != RA_OK) return st;
+  return RA_OK;
+}
+
+ra_status check_state_mem(float* m, float* l, float* acc) {
+  ra_status st;
+  if ((st = check_mem(m, false, "m")) != RA_OK) return st;
+  if ((st = check_mem(l, false, "l")) != RA_OK) return st;
+  if ((st = check_mem(acc, false, "acc")) != RA_OK) return st;
+  return RA_OK;
+}
+
+// Per-thread events of the host-streamed path, created on first use and kept
+// for the life of the thread (not destroyed at exit, when the runtime may
+// already be gone).
+struct StreamEvents {
+  hipEvent_t full[2] = {nullptr, nullptr};
+  hipEvent_t free_[2] = {nullptr, nullptr};
+  hipEvent_t start = nullptr;
+  bool ready = false;
+};
+thread_local StreamEvents g_ev;
+
+hipError_t events_ready() {
+  if (g_ev.ready) return hipSuccess;
+  hipError_t e;
+  for (int i = 0; i < 2; ++i) {
+    if ((e = hipEventCreateWithFlags(&g_ev.full[i], hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&g_ev.free_[i], hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  if ((e = hipEventCreateWithFlags(&g_ev.start, hipEventDisableTiming)) != hipSuccess) return e;
+  g_ev.ready = true;
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ringattn_abi_version(void) { return RINGATTN_ABI_VERSION; }
+
+const char* ringattn_status_str(int status) {
+  switch (status) {
+    case RA_OK: return "RA_OK";
+    case RA_E_NULL: return "RA_E_NULL: required pointer is NULL";
+    case RA_E_SHAPE: return "RA_E_SHAPE: invalid sizes or strides";
+    case RA_E_DTYPE: return "RA_E_DTYPE: unsupported dtype pair";
+    case RA_E_ALIGN: return "RA_E_ALIGN: pointer or row not 16-byte aligned";
+    case RA_E_UNSUPPORTED: return "RA_E_UNSUPPORTED: outside what the kernels implement";
+    case RA_E_MEMTYPE: return "RA_E_MEMTYPE: wrong kind of memory";
+    case RA_E_HIP: return "RA_E_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ringattn_last_error(void) { return g_err.c_str(); }
+
+ra_status ringattn_ring_order(int32_t q_idx, int32_t num_devices, int32_t* order) {
+  g_err.clear();
+  if (!order) return fail(RA_E_NULL, "order is NULL");
+  if (num_devices < 1) return fail(RA_E_SHAPE, "num_devices must be >= 1");
+  if (q_idx < 0 || q_idx >= num_devices) return fail(RA_E_SHAPE, "q_idx must be in [0, num_devices)");
+  for (int32_t s = 0; s < num_devices; ++s) order[s] = ((q_idx - s) % num_devices + num_devices) % num_devices;
+  return RA_OK;
+}
+
+int32_t ringattn_block_class(const ra_desc* desc, int64_t kv_pos0) {
+  if (!desc) return -1;
+  return classify(desc, kv_pos0);
+}
+
+ra_status ringattn_init_state(const ra_desc* desc, float* m, float* l, float* acc, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_desc(desc)) != RA_OK) return st;
+  if (desc->q_len == 0) return RA_OK;  // empty query chunk: nothing to do
+  if ((st = check_state_ptrs(m, l, acc)) != RA_OK) return st;
+  if ((st = check_state_mem(m, l, acc)) != RA_OK) return st;
+  const int64_t rows = (int64_t)desc->batch * desc->heads * desc->q_len;
+  hipError_t e = ra::launch_init_state(rows, desc->head_dim, m, l, acc, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "init_state launch");
+}
+
+ra_status ringattn_block_fwd(const ra_desc* desc, const void* q, const void* k, const void* v, int64_t kv_pos0,
+                             float* m, float* l, float* acc, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_desc(desc)) != RA_OK) return st;
+  if (desc->q_len == 0 || desc->kv_len == 0) return RA_OK;  // nothing to attend
+  if ((st = need_ptr(q, "q")) != RA_OK) return st;
+  if ((st = need_ptr(k, "k")) != RA_OK) return st;
+  if ((st = need_ptr(v, "v")) != RA_OK) return st;
+  if ((st = check_state_ptrs(m, l, acc)) != RA_OK) return st;
+  if ((st = check_mem(q, false, "q")) != RA_OK) return st;
+  if ((st = check_mem(k, false, "k")) != RA_OK) return st;
+  if ((st = check_mem(v, false, "v")) != RA_OK) return st;
+  if ((st = check_state_mem(m, l, acc)) != RA_OK) return st;
+  if (classify(desc, kv_pos0) == RA_BLOCK_SKIP) return RA_OK;
+  BlockTable t;
+  std::memset(&t, 0, sizeof t);
+  t.k[0] = k;
+  t.v[0] = v;
+  t.pos0[0] = kv_pos0;
+  AttnArgs a = make_args(desc, q, nullptr, nullptr, m, l, acc);
+  hipError_t e = launch_attn(desc, a, t, 1, ra::kLoadStore, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "block kernel launch");
+}
+
+ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l, const float* acc, void* o,
+                            float* lse, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_desc(desc)) != RA_OK) return st;
+  if (desc->q_len == 0) return RA_OK;  // empty query chunk: nothing to do
+  if ((st = check_state_ptrs((float*)m, (float*)l, (float*)acc)) != RA_OK) return st;
+  if ((st = need_ptr(o, "o")) != RA_OK) return st;
+  if ((st = need_ptr(lse, "lse")) != RA_OK) return st;
+  if ((st = check_state_mem((float*)m, (float*)l, (float*)acc)) != RA_OK) return st;
+  if ((st = check_mem(o, false, "o")) != RA_OK) return st;
+  if ((st = check_mem(lse, false, "lse")) != RA_OK) return st;
+  AttnArgs a = make_args(desc, nullptr, o, lse, (float*)m, (float*)l, (float*)acc);
+  hipError_t e = ra::launch_finalize(a, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "finalize launch");
+}
+
+ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* const* k_blocks,
+                            const void* const* v_blocks, const int64_t* kv_pos0, int32_t num_blocks,
+                            int32_t kv_on_host, void* const* stage_k, void* const* stage_v, float* m, float* l,
+                            float* acc, void* o, float* lse, hipStream_t compute, hipStream_t copy) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_desc(desc)) != RA_OK) return st;
+  if (num_blocks < 0) return fail(RA_E_SHAPE, "num_blocks must be >= 0");
+  if (kv_on_host != 0 && kv_on_host != 1) return fail(RA_E_SHAPE, "kv_on_host must be 0 or 1");
+  if (desc->q_len == 0) return RA_OK;  // empty query chunk: nothing to do
+  if ((st = need_ptr(q, "q")) != RA_OK) return st;
+  if ((st = need_ptr(o, "o")) != RA_OK) return st;
+  if ((st = need_ptr(lse, "lse")) != RA_OK) return st;
+  if (num_blocks > 0 && (!k_blocks || !v_blocks || !kv_pos0))
+    return fail(RA_E_NULL, "k_blocks, v_blocks and kv_pos0 are required when num_blocks > 0");
+
+  // Blocks that some row can see, in the given order.
+  std::vector<int> live;
+  live.reserve(num_blocks);
+  for (int i = 0; i < num_blocks; ++i) {
+    if ((st = need_ptr(k_blocks[i], "k_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(v_blocks[i], "v_blocks[i]")) != RA_OK) return st;
+    if (classify(desc, kv_pos0[i]) != RA_BLOCK_SKIP) live.push_back(i);
+  }
+  const bool perblock = kv_on_host || (desc->flags & RA_FLAG_PERBLOCK);
+  const bool needs_ws = perblock || (int)live.size() > RA_FUSED_MAX_BLOCKS;
+  if (needs_ws && (st = check_state_ptrs(m, l, acc)) != RA_OK) return st;
+  const int64_t block_bytes =
+      (int64_t)desc->batch * desc->kv_len * desc->heads * desc->head_dim * esize(desc->in_dtype);
+  if (kv_on_host) {
+    if (!stage_k || !stage_v) return fail(RA_E_NULL, "stage_k and stage_v are required when kv_on_host = 1");
+    for (int i = 0; i < 2; ++i) {
+      if ((st = need_ptr(stage_k[i], "stage_k[i]")) != RA_OK) return st;
+      if ((st = need_ptr(stage_v[i], "stage_v[i]")) != RA_OK) return st;
+    }
+    if (copy == compute) return fail(RA_E_SHAPE, "copy stream must differ from the compute stream");
+    const int64_t hd = (int64_t)desc->heads * desc->head_dim;
+    if (desc->kv_stride[2] != desc->head_dim || desc->kv_stride[1] != hd ||
+        (desc->batch > 1 && desc->kv_stride[0] != desc->kv_len * hd))
+      return fail(RA_E_UNSUPPORTED, "host-resident blocks must be densely packed [B, Ck, H, D]");
+  }
+
+  // Memory kinds (HIP).
+  if ((st = check_mem(q, false, "q")) != RA_OK) return st;
+  if ((st = check_mem(o, false, "o")) != RA_OK) return st;
+  if ((st = check_mem(lse, false, "lse")) != RA_OK) return st;
+  if (needs_ws && (st = check_state_mem(m, l, acc)) != RA_OK) return st;
+  for (int i : live) {
+    if ((st = check_mem(k_blocks[i], kv_on_host == 1, "k_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(v_blocks[i], kv_on_host == 1, "v_blocks[i]")) != RA_OK) return st;
+  }
+  if (kv_on_host) {
+    for (int i = 0; i < 2; ++i) {
+      if ((st = check_mem(stage_k[i], false, "stage_k[i]")) != RA_OK) return st;
+      if ((st = check_mem(stage_v[i], false, "stage_v[i]")) != RA_OK) return st;
+    }
+  }
+
+  AttnArgs a = make_args(desc, q, o, lse, m, l, acc);
+  BlockTable t;
+  std::memset(&t, 0, sizeof t);
+  hipError_t e;
+  const int64_t rows = (int64_t)desc->batch * desc->heads * desc->q_len;
+
+  if (!perblock) {
+    // Fused: state on chip for up to RA_FUSED_MAX_BLOCKS blocks per launch.
+    const int nlive = (int)live.size();
+    if (nlive <= RA_FUSED_MAX_BLOCKS) {
+      for (int j = 0; j < nlive; ++j) {
+        t.k[j] = k_blocks[live[j]];
+        t.v[j] = v_blocks[live[j]];
+        t.pos0[j] = kv_pos0[live[j]];
+      }
+      e = launch_attn(desc, a, t, nlive, ra::kInitFinalize, compute);
+      return e == hipSuccess ? RA_OK : hip_fail(e, "fused kernel launch");
+    }
+    for (int s0 = 0; s0 < nlive; s0 += RA_FUSED_MAX_BLOCKS) {
+      const int n = (nlive - s0 < RA_FUSED_MAX_BLOCKS) ? nlive - s0 : RA_FUSED_MAX_BLOCKS;
+      for (int j = 0; j < n; ++j) {
+        t.k[j] = k_blocks[live[s0 + j]];
+        t.v[j] = v_blocks[live[s0 + j]];
+        t.pos0[j] = kv_pos0[live[s0 + j]];
+      }
+      const bool first = s0 == 0, last = s0 + n >= nlive;
+      const int mode = first ? ra::kInitStore : (last ? ra::kLoadFinalize : ra::kLoadStore);
+      e = launch_attn(desc, a, t, n, mode, compute);
+      if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+    }
+    return RA_OK;
+  }
+
+  // Per-block: init, one launch per live block with the state in HBM, finalize.
+  e = ra::launch_init_state(rows, desc->head_dim, m, l, acc, compute);
+  if (e != hipSuccess) return hip_fail(e, "init_state launch");
+  if (!kv_on_host) {
+    for (int i : live) {
+      t.k[0] = k_blocks[i];
+      t.v[0] = v_blocks[i];
+      t.pos0[0] = kv_pos0[i];
+      e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
+      if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+    }
+  } else {
+    // Two staging slots: block s goes to slot s % 2.  The copy of block s
+    // waits until the kernel of block s-2 (same slot) has finished; the
+    // kernel of block s waits until its copy has landed.
+    if ((e = events_ready()) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventRecord(g_ev.start, compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    if ((e = hipStreamWaitEvent(copy, g_ev.start, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    for (size_t s = 0; s < live.size(); ++s) {
+      const int i = live[s];
+      const int slot = (int)(s & 1);
+      if (s >= 2 && (e = hipStreamWaitEvent(copy, g_ev.free_[slot], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      if ((e = hipMemcpyAsync(stage_k[slot], k_blocks[i], block_bytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync K");
+      if ((e = hipMemcpyAsync(stage_v[slot], v_blocks[i], block_bytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
+        return hip_fail(e, "hipMemcpyAsync V");
+      if ((e = hipEventRecord(g_ev.full[slot], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+      if ((e = hipStreamWaitEvent(compute, g_ev.full[slot], 0)) != hipSuccess)
+        return hip_fail(e, "hipStreamWaitEvent");
+      t.k[0] = stage_k[slot];
+      t.v[0] = stage_v[slot];
+      t.pos0[0] = kv_pos0[i];
+      e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
+      if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+      if ((e = hipEventRecord(g_ev.free_[slot], compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+  }
+  e = ra::launch_finalize(a, compute);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "finalize launch");
+}
+
+ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = need_ptr(src, "src")) != RA_OK) return st;
+  if ((st = need_ptr(dst, "dst")) != RA_OK) return st;
+  if (bytes < 0 || bytes % 16 != 0) return fail(RA_E_SHAPE, "bytes must be a non-negative multiple of 16");
+  if ((st = check_mem(src, false, "src")) != RA_OK) return st;
+  if ((st = check_mem(dst, false, "dst")) != RA_OK) return st;
+  hipError_t e = ra::launch_copy(src, dst, bytes, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "copy launch");
+}
+
+}  // extern "C"

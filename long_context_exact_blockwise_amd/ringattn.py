@@ -1,0 +1,221 @@
+"""ctypes binding over libringattn.so (argument marshalling only).
+
+Functions carry the C entry points' names.  torch tensors supply device
+pointers, strides and the current HIP stream; every step of the attention
+path runs in the library's kernels.  A missing library raises: there is no
+fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libringattn.so")
+
+RA_OK, RA_E_NULL, RA_E_SHAPE, RA_E_DTYPE, RA_E_ALIGN, RA_E_UNSUPPORTED, RA_E_MEMTYPE, RA_E_HIP = range(8)
+RA_F32, RA_BF16 = 0, 1
+RA_FLAG_PERBLOCK = 1
+RA_BLOCK_SKIP, RA_BLOCK_FULL, RA_BLOCK_DIAG = 0, 1, 2
+RA_FUSED_MAX_BLOCKS = 64
+
+SYMBOLS = (
+    "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
+    "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
+    "ringattn_ring_fwd", "ringattn_probe_copy",
+)
+
+
+class RingAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [status {status}]")
+        self.status = status
+
+
+class RaDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("q_len", ctypes.c_int64), ("kv_len", ctypes.c_int64),
+        ("q_pos0", ctypes.c_int64), ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(or python -m long_context_exact_blockwise_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(RaDesc)
+    L.ringattn_abi_version.restype = ctypes.c_int
+    L.ringattn_status_str.restype = ctypes.c_char_p
+    L.ringattn_status_str.argtypes = [ctypes.c_int]
+    L.ringattn_last_error.restype = ctypes.c_char_p
+    L.ringattn_ring_order.restype = ctypes.c_int
+    L.ringattn_ring_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]
+    L.ringattn_block_class.restype = ctypes.c_int32
+    L.ringattn_block_class.argtypes = [D, ctypes.c_int64]
+    L.ringattn_init_state.restype = ctypes.c_int
+    L.ringattn_init_state.argtypes = [D, P, P, P, P]
+    L.ringattn_block_fwd.restype = ctypes.c_int
+    L.ringattn_block_fwd.argtypes = [D, P, P, P, ctypes.c_int64, P, P, P, P]
+    L.ringattn_finalize.restype = ctypes.c_int
+    L.ringattn_finalize.argtypes = [D, P, P, P, P, P, P]
+    L.ringattn_ring_fwd.restype = ctypes.c_int
+    L.ringattn_ring_fwd.argtypes = [D, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(P), ctypes.POINTER(P),
+                                    P, P, P, P, P, P, P]
+    L.ringattn_probe_copy.restype = ctypes.c_int
+    L.ringattn_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
+    if L.ringattn_abi_version() != 1:
+        raise RuntimeError("libringattn.so ABI version mismatch")
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != RA_OK:
+        L = lib()
+        msg = L.ringattn_last_error().decode() or L.ringattn_status_str(status).decode()
+        raise RingAttnError(status, msg)
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return RA_BF16
+    if t == torch.float32:
+        return RA_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(s) -> ctypes.c_void_p:
+    if s is None:
+        s = torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(q: torch.Tensor, kv_block: torch.Tensor, o: Optional[torch.Tensor] = None, *, q_pos0: int = 0,
+              causal: bool = False, scale: float = 0.0, flags: int = 0, out_dtype=None) -> RaDesc:
+    """Descriptor from tensors in [B, S, H, D] layout (strides taken as given;
+    the D stride must be 1).  kv_block is any one KV block (all share strides)."""
+    b, sq, h, d = q.shape
+    kb, ck, kh, kd = kv_block.shape
+    if (kb, kh, kd) != (b, h, d):
+        raise ValueError("q and kv blocks must share B, H and D")
+    if q.stride(3) != 1 or kv_block.stride(3) != 1 or (o is not None and o.stride(3) != 1):
+        raise ValueError("the head_dim axis must be contiguous")
+    desc = RaDesc()
+    desc.batch, desc.heads, desc.head_dim = b, h, d
+    desc.causal = 1 if causal else 0
+    desc.q_len, desc.kv_len, desc.q_pos0 = sq, ck, q_pos0
+    desc.scale = scale
+    desc.in_dtype = _dt(q.dtype)
+    if out_dtype is None:
+        out_dtype = o.dtype if o is not None else q.dtype
+    desc.out_dtype = _dt(out_dtype)
+    desc.flags = flags
+    for i in range(3):
+        desc.q_stride[i] = q.stride(i)
+        desc.kv_stride[i] = kv_block.stride(i)
+        desc.o_stride[i] = o.stride(i) if o is not None else q.stride(i)
+    return desc
+
+
+def ringattn_ring_order(q_idx: int, num_devices: int) -> list:
+    arr = (ctypes.c_int32 * max(num_devices, 1))()
+    _check(lib().ringattn_ring_order(q_idx, num_devices, arr))
+    return list(arr)[:num_devices]
+
+
+def ringattn_block_class(desc: RaDesc, kv_pos0: int) -> int:
+    return lib().ringattn_block_class(ctypes.byref(desc), kv_pos0)
+
+
+def ringattn_init_state(desc: RaDesc, m, l, acc, stream=None):
+    _check(lib().ringattn_init_state(ctypes.byref(desc), _ptr(m), _ptr(l), _ptr(acc), _stream(stream)))
+
+
+def ringattn_block_fwd(desc: RaDesc, q, k, v, kv_pos0: int, m, l, acc, stream=None):
+    _check(lib().ringattn_block_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), kv_pos0, _ptr(m), _ptr(l),
+                                    _ptr(acc), _stream(stream)))
+
+
+def ringattn_finalize(desc: RaDesc, m, l, acc, o, lse, stream=None):
+    _check(lib().ringattn_finalize(ctypes.byref(desc), _ptr(m), _ptr(l), _ptr(acc), _ptr(o), _ptr(lse),
+                                   _stream(stream)))
+
+
+def ringattn_ring_fwd(desc: RaDesc, q, k_blocks: Sequence, v_blocks: Sequence, kv_pos0: Sequence[int], o, lse,
+                      m=None, l=None, acc=None, *, kv_on_host: bool = False, stage_k: Sequence = None,
+                      stage_v: Sequence = None, stream=None, copy_stream=None):
+    n = len(k_blocks)
+    P = ctypes.c_void_p
+    kp = (P * max(n, 1))(*[t.data_ptr() for t in k_blocks])
+    vp = (P * max(n, 1))(*[t.data_ptr() for t in v_blocks])
+    pp = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_pos0])
+    sk = sv = None
+    if stage_k is not None:
+        sk = (P * 2)(*[t.data_ptr() for t in stage_k])
+        sv = (P * 2)(*[t.data_ptr() for t in stage_v])
+    cs = _stream(copy_stream) if copy_stream is not None else None
+    _check(lib().ringattn_ring_fwd(ctypes.byref(desc), _ptr(q), kp, vp, pp, n, 1 if kv_on_host else 0, sk, sv,
+                                   _ptr(m), _ptr(l), _ptr(acc), _ptr(o), _ptr(lse), _stream(stream), cs))
+
+
+def ringattn_probe_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
+    _check(lib().ringattn_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+# ---- convenience wrappers (allocation of outputs / workspace with torch) ----
+
+def state_buffers(desc: RaDesc, device):
+    rows = (desc.batch, desc.heads, desc.q_len)
+    m = torch.empty(rows, dtype=torch.float32, device=device)
+    l = torch.empty(rows, dtype=torch.float32, device=device)
+    acc = torch.empty(rows + (desc.head_dim,), dtype=torch.float32, device=device)
+    return m, l, acc
+
+
+def ring_forward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: Sequence[torch.Tensor],
+                 kv_pos0: Sequence[int], *, q_pos0: int = 0, causal: bool = False, scale: float = 0.0,
+                 perblock: bool = False, out_dtype=None, o=None, lse=None, workspace=None):
+    """Attention of q over the blocks (device tensors) in the given order.
+    Returns (O [B, Sq, H, D], LSE [B, H, Sq] fp32)."""
+    out_dtype = out_dtype or q.dtype
+    b, sq, h, d = q.shape
+    if o is None:
+        o = torch.empty((b, sq, h, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
+    desc = make_desc(q, k_blocks[0] if len(k_blocks) else q, o, q_pos0=q_pos0, causal=causal, scale=scale,
+                     flags=RA_FLAG_PERBLOCK if perblock else 0)
+    if len(k_blocks) == 0:
+        desc.kv_len = 0
+    need_ws = perblock or len(k_blocks) > RA_FUSED_MAX_BLOCKS
+    m = l = acc = None
+    if need_ws:
+        m, l, acc = workspace if workspace is not None else state_buffers(desc, q.device)
+    ringattn_ring_fwd(desc, q, k_blocks, v_blocks, kv_pos0, o, lse, m, l, acc)
+    return o, lse
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,150 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, its host-only helpers are right, and invalid calls return
+their status before any HIP call (fake pointers are never dereferenced)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from long_context_exact_blockwise_amd import ringattn as ra
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ringattn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ra.LIB_PATH), reason="libringattn.so not built")
+
+
+def header_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ringattn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = ra.lib()
+    declared = header_symbols()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(ra.SYMBOLS) == declared
+
+
+def test_abi_version_and_status_strings():
+    L = ra.lib()
+    assert L.ringattn_abi_version() == 1
+    for st in range(8):
+        assert L.ringattn_status_str(st).startswith(b"RA_")
+
+
+def test_ring_order_definition():
+    # device q_idx at step s holds the block of device (q_idx - s) mod P
+    for p in (1, 2, 4, 8, 128):
+        for q_idx in sorted({0, 1 % p, p // 2, p - 1}):
+            assert ra.ringattn_ring_order(q_idx, p) == [(q_idx - s) % p for s in range(p)]
+    with pytest.raises(ra.RingAttnError) as e:
+        ra.ringattn_ring_order(4, 4)
+    assert e.value.status == ra.RA_E_SHAPE
+
+
+def _desc(**kw):
+    d = ra.RaDesc()
+    d.batch, d.heads, d.head_dim, d.causal = kw.get("batch", 1), kw.get("heads", 2), kw.get("head_dim", 128), \
+        kw.get("causal", 1)
+    d.q_len, d.kv_len, d.q_pos0 = kw.get("q_len", 256), kw.get("kv_len", 256), kw.get("q_pos0", 512)
+    d.scale = kw.get("scale", 0.0)
+    d.in_dtype, d.out_dtype = kw.get("in_dtype", ra.RA_BF16), kw.get("out_dtype", ra.RA_BF16)
+    d.flags = kw.get("flags", 0)
+    hd = d.heads * d.head_dim
+    for arr, s in ((d.q_stride, kw.get("q_stride")), (d.kv_stride, kw.get("kv_stride")),
+                   (d.o_stride, kw.get("o_stride"))):
+        st = s or (d.q_len * hd, hd, d.head_dim)
+        for i in range(3):
+            arr[i] = st[i]
+    return d
+
+
+def test_block_class():
+    d = _desc(q_len=256, kv_len=256, q_pos0=512)
+    assert ra.ringattn_block_class(d, 0) == ra.RA_BLOCK_FULL       # keys 0..255 <= rows 512..
+    assert ra.ringattn_block_class(d, 256) == ra.RA_BLOCK_FULL     # last key 511 < first row 512
+    assert ra.ringattn_block_class(d, 257) == ra.RA_BLOCK_FULL     # last key 512 = first row (inclusive)
+    assert ra.ringattn_block_class(d, 258) == ra.RA_BLOCK_DIAG     # last key 513 is after row 512
+    assert ra.ringattn_block_class(d, 512) == ra.RA_BLOCK_DIAG
+    assert ra.ringattn_block_class(d, 767) == ra.RA_BLOCK_DIAG     # first key 767 = last row
+    assert ra.ringattn_block_class(d, 768) == ra.RA_BLOCK_SKIP
+    d.causal = 0
+    assert ra.ringattn_block_class(d, 10 ** 9) == ra.RA_BLOCK_FULL
+    d.kv_len = 0
+    assert ra.ringattn_block_class(d, 0) == ra.RA_BLOCK_SKIP
+    assert ra.lib().ringattn_block_class(None, 0) == -1
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: validation fails before any access
+
+
+def _ring(d, q=FAKE, o=FAKE, lse=FAKE, kb=(FAKE,), vb=(FAKE,), pos=(0,), on_host=0, stage=None, m=None,
+          l=None, acc=None, copy=None, compute=None):
+    L = ra.lib()
+    P = ctypes.c_void_p
+    n = len(kb) if kb is not None else len(vb)
+    karr = (P * max(n, 1))(*kb) if kb is not None else None
+    varr = (P * max(n, 1))(*vb) if vb is not None else None
+    parr = (ctypes.c_int64 * max(n, 1))(*pos)
+    sk = (P * 2)(*stage) if stage else None
+    sv = (P * 2)(*stage) if stage else None
+    st = L.ringattn_ring_fwd(ctypes.byref(d) if d is not None else None, q, karr, varr, parr, n, on_host, sk, sv,
+                             m, l, acc, o, lse, compute, copy)
+    return st, L.ringattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), ra.RA_E_UNSUPPORTED),
+    (dict(head_dim=256), ra.RA_E_UNSUPPORTED),
+    (dict(batch=0), ra.RA_E_SHAPE),
+    (dict(heads=0), ra.RA_E_SHAPE),
+    (dict(q_len=-1), ra.RA_E_SHAPE),
+    (dict(kv_len=-5), ra.RA_E_SHAPE),
+    (dict(causal=2), ra.RA_E_SHAPE),
+    (dict(scale=float("nan")), ra.RA_E_SHAPE),
+    (dict(in_dtype=ra.RA_F32, out_dtype=ra.RA_BF16), ra.RA_E_DTYPE),
+    (dict(in_dtype=7), ra.RA_E_DTYPE),
+    (dict(q_stride=(256 * 256, 256, 100)), ra.RA_E_ALIGN),   # 200 bytes: rows not 16-byte aligned
+    (dict(kv_stride=(256 * 256, 0, 128)), ra.RA_E_SHAPE),    # zero stride along a dim of size > 1
+    (dict(kv_stride=(256 * 256, 1 << 24, 128)), ra.RA_E_UNSUPPORTED),
+    (dict(flags=4), ra.RA_E_UNSUPPORTED),
+])
+def test_descriptor_rejected_before_enqueue(kw, status):
+    st, msg = _ring(_desc(**kw))
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_pointer_checks_before_enqueue():
+    d = _desc()
+    assert _ring(None)[0] == ra.RA_E_NULL
+    assert _ring(d, q=None)[0] == ra.RA_E_NULL
+    assert _ring(d, o=FAKE + 8)[0] == ra.RA_E_ALIGN
+    assert _ring(d, kb=(FAKE + 4,))[0] == ra.RA_E_ALIGN
+    assert _ring(d, kb=None)[0] == ra.RA_E_NULL
+    assert _ring(d, on_host=2)[0] == ra.RA_E_SHAPE
+    # host-streamed needs staging slots, a workspace, and two streams
+    assert _ring(d, on_host=1)[0] == ra.RA_E_NULL
+    st, msg = _ring(d, on_host=1, stage=(FAKE, FAKE), m=FAKE, l=FAKE, acc=FAKE)
+    assert st == ra.RA_E_SHAPE and "stream" in msg
+    d2 = _desc(flags=ra.RA_FLAG_PERBLOCK)
+    assert _ring(d2)[0] == ra.RA_E_NULL  # per-block path needs the state workspace
+    L = ra.lib()
+    assert L.ringattn_block_fwd(ctypes.byref(d), FAKE, None, FAKE, 0, FAKE, FAKE, FAKE, None) == ra.RA_E_NULL
+    assert L.ringattn_finalize(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE + 2, FAKE, None) == ra.RA_E_ALIGN
+    assert L.ringattn_init_state(ctypes.byref(d), None, FAKE, FAKE, None) == ra.RA_E_NULL
+    assert L.ringattn_probe_copy(FAKE, FAKE, 15, None) == ra.RA_E_SHAPE
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error path")
+def test_valid_call_without_device_reports_hip_error():
+    st, msg = _ring(_desc())
+    assert st in (ra.RA_E_HIP, ra.RA_E_MEMTYPE), (st, msg)
+    assert msg
