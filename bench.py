@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark: one device's share of a causal ring-attention forward on one MI355X.
+
+A step is one whole ring pass (every KV block of the ring attended and merged,
+O and LSE written) over the workload's synthetic inputs, which are resident in
+HBM before timing starts.  Default workload: 16 heads, head_dim 128, local
+query chunk 131072 rows (512K tokens over a ring of 4), 4 KV blocks of 131072
+keys, causal with the chunk at ring index 3, bf16 in / fp32 accumulate.
+
+Prints ONE JSON line.  `value` is causal-adjusted TFLOP/s: 4*B*H*D*(visible
+query-key pairs) per step over the measured step time.  `roofline` prices the
+fused attention kernel's live-measured duration (HIP events on the launch
+stream) against the bf16 dense MFMA peak.  `cpu_baseline` times the fp64 CPU
+oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+       [--perblock] [--no-cpu-baseline] [--traffic-calib]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal-adjusted attention TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 flop/clk/CU x 2.4 GHz (AMD's published 2.5 PF)
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "long_context_exact_blockwise_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_fused_causal_q131072_p4_traffic.txt")
+
+
+def visible_pairs(wl) -> int:
+    """Query-key pairs with the key visible to the query, one head: a key at
+    position p is visible to a query at position t iff p <= t (causal), all
+    pairs otherwise."""
+    total = 0
+    q0, q1 = wl.q_pos0, wl.q_pos0 + wl.q_len - 1
+    for j in range(wl.num_blocks):
+        k0 = wl.kv_pos0(j)
+        k1 = k0 + wl.kv_len - 1
+        if not wl.causal:
+            total += wl.q_len * wl.kv_len
+            continue
+        # rows t >= k1 see the whole block
+        full_from = max(q0, k1)
+        if full_from <= q1:
+            total += (q1 - full_from + 1) * wl.kv_len
+        # rows k0 <= t < k1 see t - k0 + 1 keys
+        lo, hi = max(q0, k0), min(q1, k1 - 1)
+        if hi >= lo:
+            n = hi - lo + 1
+            total += n * (lo - k0 + 1) + n * (n - 1) // 2
+    return total
+
+
+def flops(wl) -> int:
+    return 4 * wl.batch * wl.heads * wl.head_dim * visible_pairs(wl)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or None when
+    missing or taken on a different kernel source."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_hash():
+            return None
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, wl, o, lse, heads=None, extra_rows=94):
+    """Time the fp64 oracle on sampled rows of every head; also check those
+    rows against the GPU output at the bf16 tolerances."""
+    import numpy as np
+    import oracle
+    from long_context_exact_blockwise_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    heads = list(range(wl.heads)) if heads is None else heads
+    rows = inputs.sample_rows(wl.q_len, extra=extra_rows, seed=1)
+    rows_np = np.asarray(rows)
+    k_host = x.k.cpu()
+    v_host = x.v.cpu()
+    q_host = x.q.cpu()
+    o_host = o.float().cpu().numpy()
+    lse_host = lse.cpu().numpy()
+    t_oracle = 0.0
+    err_o = 0.0
+    err_l = 0.0
+    scale_o = 0.0
+    pos = [wl.kv_pos0(j) for j in range(wl.num_blocks)]
+    for h in heads:
+        q64 = q_host[:, :, h:h + 1, :].float().double().numpy()
+        kb = [k_host[:, j * wl.kv_len:(j + 1) * wl.kv_len, h:h + 1, :].float().double().numpy()
+              for j in range(wl.num_blocks)]
+        vb = [v_host[:, j * wl.kv_len:(j + 1) * wl.kv_len, h:h + 1, :].float().double().numpy()
+              for j in range(wl.num_blocks)]
+        t0 = time.perf_counter()
+        ro, rl = oracle.ring_attention(q64, kb, vb, wl.q_pos0, pos, wl.causal, rows=rows_np)
+        t_oracle += time.perf_counter() - t0
+        go = o_host[:, rows_np, h:h + 1, :]
+        gl = lse_host[:, h:h + 1, rows_np]
+        err_o = max(err_o, float(np.abs(go - ro).max()))
+        err_l = max(err_l, float((np.abs(gl - rl) / np.maximum(1.0, np.abs(rl))).max()))
+        scale_o = max(scale_o, float(np.abs(ro).max()))
+    # algorithmic flops of the sampled rows (visible keys per row x 4D)
+    n_vis = 0
+    for r in rows:
+        t = wl.q_pos0 + r
+        for j in range(wl.num_blocks):
+            k0 = wl.kv_pos0(j)
+            n_vis += wl.kv_len if not wl.causal else max(0, min(wl.kv_len, t - k0 + 1))
+    f = 4 * wl.head_dim * n_vis * len(heads)
+    value = f / t_oracle / 1e12
+    per_pair = t_oracle / (n_vis * len(heads))
+    base = {
+        "value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"{len(rows)} query rows (first, last, {extra_rows} seeded) x {len(heads)} heads of the same workload, "
+                  f"fp64 NumPy, {t_oracle:.1f} s; full-workload extrapolation "
+                  f"{per_pair * visible_pairs(wl) * wl.heads * wl.batch / 3600:.0f} h",
+    }
+    tol_ok = err_o <= 2e-2 and err_l <= 1e-3 and (scale_o == 0 or err_o <= 1e-2 * scale_o)
+    parity = {"rows": len(rows) * len(heads), "max_abs_o": err_o, "max_rel_lse": err_l,
+              "max_abs_o_over_max_o": err_o / scale_o if scale_o else 0.0, "pass": bool(tol_ok)}
+    return base, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--perblock", action="store_true", help="per-block path instead of the fused kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-calib", action="store_true",
+                    help="also run one 1 GiB plain copy kernel (byte-counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one device's share of the ring on ONE GPU; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: the inter-device ring is out of scope.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_exact_blockwise_amd import inputs
+    from long_context_exact_blockwise_amd import ringattn as ra
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    ra.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    wl = inputs.CONFIGS[args.workload]
+    x = inputs.make_inputs(wl, dev, seed=0)
+    order = ra.ringattn_ring_order(wl.q_idx, wl.num_blocks)
+    kb = [x.k_block(j) for j in order]
+    vb = [x.v_block(j) for j in order]
+    pos = [wl.kv_pos0(j) for j in order]
+    o = torch.empty_like(x.q)
+    lse = torch.empty((wl.batch, wl.heads, wl.q_len), dtype=torch.float32, device=dev)
+    perblock = args.perblock or wl.host_streamed
+    desc = ra.make_desc(x.q, kb[0], o, q_pos0=wl.q_pos0, causal=wl.causal,
+                        flags=ra.RA_FLAG_PERBLOCK if perblock else 0)
+    ws = ra.state_buffers(desc, dev) if (perblock or len(kb) > ra.RA_FUSED_MAX_BLOCKS) else (None, None, None)
+
+    extra = {}
+    if wl.host_streamed:
+        hk = [t.cpu().pin_memory() for t in kb]
+        hv = [t.cpu().pin_memory() for t in vb]
+        stage_k = [torch.empty_like(kb[0]).contiguous() for _ in range(2)]
+        stage_v = [torch.empty_like(vb[0]).contiguous() for _ in range(2)]
+        copy_stream = torch.cuda.Stream()
+        hdesc = ra.make_desc(x.q, hk[0], o, q_pos0=wl.q_pos0, causal=wl.causal)
+
+        def step():
+            ra.ringattn_ring_fwd(hdesc, x.q, hk, hv, pos, o, lse, *ws, kv_on_host=True, stage_k=stage_k,
+                                 stage_v=stage_v, copy_stream=copy_stream)
+    else:
+        def step():
+            ra.ringattn_ring_fwd(desc, x.q, kb, vb, pos, o, lse, *ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K back-to-back steps, events around each for the kernel
+    # durations (same stream as the launches: torch's current stream).
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        step()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    ev_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_ms = sum(ev_ms) / len(ev_ms)
+    f = flops(wl)
+    value = f / (ms_step * 1e-3) / 1e12
+    achieved = f / (kern_ms * 1e-3) / 1e12
+    finite = bool(torch.isfinite(o.float()).all().item())
+
+    if wl.host_streamed:
+        # Overlap: resident per-block time, copy-only time, streamed time.
+        def resident():
+            ra.ringattn_ring_fwd(desc, x.q, kb, vb, pos, o, lse, *ws)
+        for _ in range(2):
+            resident()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            resident()
+        torch.cuda.synchronize()
+        t_res = (time.perf_counter() - t1) / args.steps
+        nbytes = sum(t.numel() * t.element_size() for t in hk + hv)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            for i in range(len(hk)):
+                stage_k[i % 2].copy_(hk[i], non_blocking=True)
+                stage_v[i % 2].copy_(hv[i], non_blocking=True)
+        torch.cuda.synchronize()
+        t_copy = (time.perf_counter() - t1) / args.steps
+        t_str = ms_step * 1e-3
+        eta = (t_res + t_copy - t_str) / min(t_res, t_copy)
+        extra["host_streamed"] = {
+            "t_streamed_ms": t_str * 1e3, "t_resident_ms": t_res * 1e3, "t_copy_ms": t_copy * 1e3,
+            "h2d_GBps": nbytes / t_copy / 1e9, "h2d_bytes": nbytes,
+            "fraction_of_h2d_bw": (nbytes / t_str) / (nbytes / t_copy),
+            "overlap_efficiency": max(0.0, min(1.0, eta)),
+            "note": "overlap = (T_resident + T_copy - T_streamed) / min(T_resident, T_copy); the PCIe-inclusive "
+                    "rate is `value`; fraction_of_h2d_bw = achieved H2D rate during the streamed pass over the "
+                    "copy-only rate",
+        }
+
+    if args.traffic_calib:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty(n, dtype=torch.uint8, device=dev)
+        ra.ringattn_probe_copy(src, dst, n)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = read_traffic() if not perblock else None
+    roofline = {
+        "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+        "kernel": "attn_bf16_kernel (fused ring pass)" if not perblock else "attn_bf16_kernel (per block)",
+        "launches_per_step": 1 if (not perblock and len(kb) <= ra.RA_FUSED_MAX_BLOCKS) else None,
+        "algorithmic_flop_per_step": f,
+    }
+    if wl.dtype != "bf16":
+        roofline.update(bound="latency", peak=None, frac=None)
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded iid Gaussian, resident in HBM)",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "heads": wl.heads, "head_dim": wl.head_dim,
+            "q_len": wl.q_len, "kv_len": wl.kv_len, "num_blocks": wl.num_blocks, "causal": wl.causal,
+            "q_idx": wl.q_idx, "path": "host-streamed per-block" if wl.host_streamed else
+            ("per-block" if perblock else "fused"),
+        },
+        "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "kernel_ms": kern_ms,
+        "roofline": roofline,
+        "outputs_finite": finite,
+    }
+    result.update(extra)
+    if not args.no_cpu_baseline:
+        # bound the sample to ~10-30 s of CPU work: every head of the 16-head
+        # workloads, every fourth head of the 32-head one
+        heads = list(range(wl.heads)) if wl.heads <= 16 else list(range(0, wl.heads, wl.heads // 8))
+        base, parity = cpu_baseline(x, wl, o, lse, heads=heads)
+        result["cpu_baseline"] = base
+        result["parity_sampled"] = parity
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
