@@ -86,7 +86,7 @@ typedef struct ra_desc {
   int32_t head_dim;    /* D: 64 or 128                                        */
   int32_t causal;      /* 1: key visible iff kv_pos <= q_pos; 0: all visible   */
   int64_t q_len;       /* Sq >= 0: rows of the local query chunk              */
-  int64_t kv_len;      /* Ck >= 0: keys per KV block (all blocks equal)        */
+  int64_t kv_len;      /* Ck >= 0: keys per KV block (all blocks equal), < 2^30 */
   int64_t q_pos0;      /* global position of query row 0 (q_idx * Sq)         */
   float scale;         /* softmax temperature; <= 0 selects 1/sqrt(D)         */
   int32_t in_dtype;    /* ra_dtype of Q, K, V                                 */

@@ -21,6 +21,8 @@
 // the two 32-lane halves) and the S^T result registers are directly the P^T
 // operand of the second product once the keys inside each 16-key step are
 // permuted the same way on the V side.
+#include <type_traits>
+
 #include "ra_internal.h"
 
 namespace ra {
@@ -28,6 +30,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -74,6 +77,114 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Hide a value from loop-invariant code motion: the compiler must recompute
+// whatever is derived from the result where it is used, instead of keeping
+// every derived address live in registers across the loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Row-sum bound of one tile under a stale reference: while every p of the
+// tile stays <= 2^12 the reference may lag the running max.
+constexpr float kPLim = 4096.0f;
+
+// One online-softmax step for the 32 raw scores q.k (two f32x16 fragments of
+// S^T) this lane holds for its query row; the other 32 keys of the tile sit in
+// the lane 32 away, which holds the same row.
+//
+// The state is (m2, l, acc) with m2 a reference point in log2 units: l and acc
+// are sums of exp2(s*c - m2).  Any m2 gives the same acc/l and m2 + log2 l, so
+// m2 is moved only when it must be: the tile is first exponentiated against
+// the current m2, and only if some lane of the wave then sees a row sum above
+// kPLim (the max has grown by more than 12 in log2 units, or overflowed), or
+// still has no reference (m2 = -inf), is m2 raised to the running max, the
+// tile exponentiated again and acc, l rescaled.  m2 never exceeds the running
+// max (it is only ever set to it), so l >= 1 once a key was seen.
+//
+// Writes the bf16 pairs p[q] = (p_{2q}, p_{2q+1}) that the P.V product uses
+// and adds their sum (of the same bf16 values) to lpart.
+template <int DB>
+__device__ __forceinline__ void softmax_step(const f32x16 (&s)[2], float c2, float& m2, float& lpart,
+                                             f32x16 (&acc)[DB], bf16x2 (&p)[16]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  auto expo = [&](float mref) -> float {
+    float rsq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = 2 * q;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c2, -mref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][(e & 15) + 1], c2, -mref));
+      p[q] = bf16x2{(__bf16)p0, (__bf16)p1};
+      rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p[q], ones, rsq[q & 3], false);
+    }
+    return (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
+  };
+  float rs = expo(m2 == -INFINITY ? 0.f : m2);
+  if (__any(!(rs <= kPLim) || m2 == -INFINITY)) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m2, mx * c2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
+    m2 = m_new;
+    rs = expo(m_use);
+    lpart *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+  }
+  lpart += rs;
+}
+
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// i's bytes land at lds_dst + 16 i.  base and lds_dst are wave-uniform.  The
+// copy is issued from inline assembly so that the compiler does not track it:
+// its own tracking would wait for every copy in flight before the next LDS
+// read of any buffer, which serialises the prefetch with the compute.  The
+// kernels wait for their copies themselves (s_waitcnt vmcnt) before the
+// barrier that publishes a buffer.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t bv = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+// LDS byte address of a generic pointer into the dynamic LDS array.
+__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: every wait a barrier needs here
+// is explicit (the copies' vmcnt; LDS reads are consumed before the barrier).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 struct RowRange {
@@ -185,19 +296,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
         ok -= shift;
         ov -= shift;
       }
-      __builtin_amdgcn_global_load_lds((const void*)(kt + ok),
-                                       (__attribute__((address_space(3))) void*)(kl + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vt + ov),
-                                       (__attribute__((address_space(3))) void*)(vl + blk * 1024), 16, 0, 0);
+      lds_dma16(kt, ok, lds_addr_of(kl) + blk * 1024);
+      lds_dma16(vt, ov, lds_addr_of(vl) + blk * 1024);
     }
   };
-  auto advance = [&](int& bi, int& t) -> bool {
-    ++t;
-    while (bi < a.nblocks && t >= block_tiles(a, tbl.pos0[bi], rr)) {
-      ++bi;
-      t = 0;
-    }
-    return bi < a.nblocks;
+  // Tile cursor over the blocks in order: block b, tile t of n visible tiles.
+  struct Cur {
+    int b, t, n;
+  };
+  auto seek = [&](Cur& c) -> bool {  // first visible tile at or after block c.b
+    while (c.b < a.nblocks && (c.n = block_tiles(a, tbl.pos0[c.b], rr)) == 0) ++c.b;
+    c.t = 0;
+    return c.b < a.nblocks;
+  };
+  auto step = [&](Cur& c) -> bool {
+    if (++c.t < c.n) return true;
+    ++c.b;
+    return seek(c);
   };
 
   // ---- per-lane LDS read bases.  K: row l32 (+32 per key block, an immediate),
@@ -222,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
   constexpr int ROWB = D * 2;  // bytes per key row in LDS
 
   const int64_t wave_first_pos = a.q_pos0 + row0 + 32 * wave;
-  int bi = 0, t = -1;
-  bool have = advance(bi, t);
+  Cur cur{0, 0, 0};
+  bool have = seek(cur);
   // A per-block launch (state in HBM) whose rows see no key of the block
   // leaves the state untouched.
   if (MODE == kLoadStore && !have) return;
@@ -245,14 +360,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     }
   }
 
-  if (have) issue_tile(bi, t, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (have) issue_tile(cur.b, cur.t, 0);
+  wait_vm<0>();
   __syncthreads();
   int buf = 0;
   while (have) {
-    int nbi = bi, nt = t;
-    const bool have_next = advance(nbi, nt);
-    if (have_next) issue_tile(nbi, nt, buf ^ 1);
+    Cur nxt = cur;
+    const bool have_next = step(nxt);
+    if (have_next) issue_tile(nxt.b, nxt.t, buf ^ 1);
+    const int bi = cur.b, t = cur.t;
 
     const int64_t t0 = (int64_t)t * BN;
     const int64_t tile_pos = tbl.pos0[bi] + t0;  // global position of the tile's key 0
@@ -260,18 +376,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     if (!wave_skip) {
       const char* kl = lds + buf * C::TILE_BYTES;
       const char* vl = lds + (2 + buf) * C::TILE_BYTES;
-      // S^T = K Q^T
+      // S^T = K Q^T.  K fragments are read two k-steps ahead of their
+      // products (the group barriers pin that order).
       f32x16 s[2];
-      s[0] = f32x16{};
-      s[1] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const bf16x8 kf = *(const bf16x8*)(kl + kbase[ks] + kb * 32 * ROWB);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int st = 0; st < 2 * C::KS - 4; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
       // mask keys past the block end and (causal) keys after this lane's row:
       // key k of the tile is live iff k < thr.
       const bool need_mask = (t0 + BN > a.kv_len) || (a.causal && tile_pos + BN - 1 > wave_first_pos);
@@ -290,34 +413,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
             if (key >= thr) s[kb][i] = -INFINITY;
           }
       }
-      // online softmax (log2 domain)
-      float mx = s[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m2, mx * c2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
-      m2 = m_new;
-      float rs = 0.f;
+      bf16x2 pp[16];
+      softmax_step<C::DB>(s, c2, m2, lpart, acc, pp);
       bf16x8 pf[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, -m_use));
-          rs += p;
-          pf[kb][i >> 3][i & 7] = (__bf16)p;
+        for (int tp = 0; tp < 2; ++tp) {
+          const int q0 = 8 * kb + 4 * tp;
+          const bf16x4 p_lo = __builtin_shufflevector(pp[q0], pp[q0 + 1], 0, 1, 2, 3);
+          const bf16x4 p_hi = __builtin_shufflevector(pp[q0 + 2], pp[q0 + 3], 0, 1, 2, 3);
+          pf[kb][tp] = __builtin_shufflevector(p_lo, p_hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
-      lpart = lpart * alpha + rs;
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      }
       // O^T += V^T P^T
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -335,13 +442,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][tp], acc[db], 0, 0, 0);
           }
         }
+      // V fragments two products ahead of their MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int st = 0; st < 4 * C::DB - 2; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vm<0>();
     __syncthreads();
     buf ^= 1;
-    bi = nbi;
-    t = nt;
+    cur = nxt;
     have = have_next;
   }
 
@@ -384,21 +499,406 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined variant: 8 waves, 256 query rows per workgroup, K/V tiles
+// shared by all eight waves.
+//
+// A wave's work on tile t is a chain: S_t = K_t Q^T, then the softmax of S_t,
+// then O += V_t P_t.  Run in that order, the matrix cores idle during the
+// softmax.  Here block t of the loop issues, interleaved instruction by
+// instruction, three independent pieces of work:
+//   O^T += V_{t-1}^T P_{t-1}^T   (16 MFMAs, P from the previous block)
+//   S_{t+1}^T = K_{t+1} Q^T      (16 MFMAs)
+//   softmax of S_t -> P_t        (vector ALU: exp2, bf16 pack, row sums)
+// so the softmax runs under the matrix products.  The (rare) move of the
+// softmax reference, with its rescale of acc, follows the interleaved part.
+//
+// LDS holds kBufs slots; slot s = (K_s, V_{s-2}) lives in buffer s % kBufs and
+// is read in block s-1.  Block t copies slot t + kBufs into the buffer of
+// slot t (read in block t-1) with direct global->LDS loads, each wave a
+// share, and waits for slot t+2 before the barrier that ends it: kBufs-2
+// slots stay in flight across barriers.  Slots past the last tile (and the V
+// part of slots 0, 1) copy a real tile whose products are discarded or
+// multiplied by P = 0, so every block issues the same number of copies and
+// the wait counts stay exact.
+constexpr int kSPWaves = 8;
+constexpr int kSPThreads = 64 * kSPWaves;
+constexpr int BMS = 32 * kSPWaves;  // query rows per workgroup
+#ifndef RA_SP_BUFS
+#define RA_SP_BUFS 4
+#endif
+constexpr int kBufs = RA_SP_BUFS;
+#ifndef RA_SP_SCHED
+#define RA_SP_SCHED 3  // interleave of the block's matrix products with its softmax: 0 compiler, 2/3 iglp strategies
+#endif
+
+template <int D>
+struct SpCfg {
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
+  static constexpr int LDS_BYTES = kBufs * SLOT_BYTES;
+  static constexpr int DPW = TILE_BYTES / 1024 / kSPWaves;  // 1 KiB copies per wave per K (or V) tile
+};
+
+template <int D, typename OutT, int MODE>
+__global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a, BlockTable tbl) {
+  using C = Cfg<D>;
+  using SC = SpCfg<D>;
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ROWB = D * 2;
+  constexpr int DPW = SC::DPW;
+
+  const int n_qt = (int)((a.q_len + BMS - 1) / BMS);
+  const int n_work = a.batch * a.heads * n_qt;
+  const int per = (n_work + 7) >> 3;
+  const int wid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (wid >= n_work) return;
+  const int bh = wid / n_qt;
+  const int qt = n_qt - 1 - (wid - bh * n_qt);
+  const int b = bh / a.heads;
+  const int h = bh - b * a.heads;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int64_t row0 = (int64_t)qt * BMS;
+  const int64_t r = row0 + 32 * wave + l32;
+  const bool row_ok = r < a.q_len;
+  RowRange rr;
+  rr.first_pos = a.q_pos0 + row0;
+  rr.last_pos = a.q_pos0 + ((row0 + BMS < a.q_len) ? row0 + BMS : a.q_len) - 1;
+  const float c2s = a.scale * kLog2e;
+  const int kv_len = (int)a.kv_len;  // < 2^30 (checked on the host)
+
+  int n_tiles = 0;
+  for (int bi = 0; bi < a.nblocks; ++bi) n_tiles += block_tiles(a, tbl.pos0[bi], rr);
+  if (MODE == kLoadStore && n_tiles == 0) return;  // leaves the state untouched
+
+  bf16x8 qf[C::KS];
+  {
+    const __bf16* qp = (const __bf16*)a.q + b * a.q_sb + r * a.q_ss + h * a.q_sh + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      if (row_ok) {
+        qf[ks] = *(const bf16x8*)(qp + 16 * ks);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qf[ks][j] = (__bf16)0.0f;
+      }
+    }
+  }
+  const int64_t sidx = ((int64_t)b * a.heads + h) * a.q_len + r;
+  float m2 = -INFINITY;
+  float lpart = 0.f;
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  if ((MODE == kLoadStore || MODE == kLoadFinalize) && row_ok) {
+    m2 = a.m[sidx] * kLog2e;
+    lpart = hf == 0 ? a.l[sidx] : 0.f;
+    const float* ap = a.acc + sidx * D + 4 * hf;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = *(const f32x4*)(ap + 32 * db + 8 * g);
+        acc[db][4 * g + 0] = v4[0];
+        acc[db][4 * g + 1] = v4[1];
+        acc[db][4 * g + 2] = v4[2];
+        acc[db][4 * g + 3] = v4[3];
+      }
+  }
+
+  if (n_tiles > 0) {
+    // ---- tile cursors (all wave-uniform, scalar): block, tile, visible tile
+    // count, position of the tile's key 0 relative to the workgroup's first
+    // row (clamped below: far-away tiles are fully visible) and, for the copy
+    // cursors, the global address of the tile for this (b, h).
+    struct Cur {
+      int b, t, n, rel;
+      const char* src;
+    };
+    const int64_t kv_head_off = ((int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh) * 2;
+    const int64_t tile_bytes_g = (int64_t)BN * a.kv_ss * 2;
+    auto seek = [&](Cur& c, int which) {  // which: 0 none, 1 K, 2 V
+      while (c.b < a.nblocks && (c.n = block_tiles(a, tbl.pos0[c.b], rr)) == 0) ++c.b;
+      c.t = 0;
+      if (c.b < a.nblocks) {
+        // visible tiles start at or before the last row; far below, clamp so
+        // that rel + 64 t stays far below for every tile of the block
+        const int64_t rel = tbl.pos0[c.b] - rr.first_pos;
+        c.rel = rel < (int64_t)INT32_MIN + 64 ? INT32_MIN + 64 : (int)rel;
+        if (which) c.src = (const char*)(which == 2 ? tbl.v[c.b] : tbl.k[c.b]) + kv_head_off;
+      }
+    };
+    auto step = [&](Cur& c, int which) {
+      if (++c.t < c.n) {
+        c.rel += BN;
+        c.src += tile_bytes_g;
+      } else {
+        ++c.b;
+        seek(c, which);
+      }
+    };
+    // The ragged tile of a block (keys past kv_len) is its last one.
+    const int ragged_t = (kv_len & (BN - 1)) ? (kv_len >> 6) : -1;
+    // Per-lane byte offsets of this wave's share of a tile: copy j moves
+    // 1 KiB = 64 lanes x 16 bytes into LDS chunk blk = wave*DPW + j; lane i
+    // fetches the global chunk that the swizzled layout puts at byte 16 i.
+    uint32_t dk[DPW], dv[DPW];
+#pragma unroll
+    for (int j = 0; j < DPW; ++j) {
+      const int slot = (wave * DPW + j) * 64 + lane;
+      const int key = slot / C::CH;
+      const int cs = slot % C::CH;
+      dk[j] = (uint32_t)(key * a.kv_ss * 2 + (k_off<D>(key, cs) / 16 - key * C::CH) * 16);
+      dv[j] = (uint32_t)(key * a.kv_ss * 2 + (v_off<D>(key, cs) / 16 - key * C::CH) * 16);
+    }
+    const uint32_t lds0 = lds_addr_of(lds) + wave * DPW * 1024;  // this wave's first chunk of a tile
+    auto copy_tile = [&](const Cur& c, bool is_v, uint32_t dst) {
+#pragma unroll
+      for (int j = 0; j < DPW; ++j) {
+        uint32_t off = is_v ? dv[j] : dk[j];
+        if (c.t == ragged_t) {  // keys past the block end re-read its last key (masked later)
+          const int key = ((wave * DPW + j) * 64 + lane) / C::CH;
+          const int last = kv_len - 1 - c.t * BN;
+          off -= (uint32_t)((key > last ? key - last : 0) * a.kv_ss * 2);
+        }
+        lds_dma16(c.src, off, dst + j * 1024);
+      }
+    };
+    // copy cursors: K of slot s is tile min(s, n-1); V of slot s is tile
+    // clamp(s-2, 0, n-1)
+    Cur ck{0, 0, 0, 0, nullptr}, cv{0, 0, 0, 0, nullptr};
+    seek(ck, 1);
+    seek(cv, 2);
+    int kidx = 0, vidx = 0;
+    auto copy_slot = [&](int s) {
+      const uint32_t dst = lds0 + (uint32_t)((s % kBufs) * SC::SLOT_BYTES);
+      copy_tile(ck, false, dst);
+      copy_tile(cv, true, dst + SC::TILE_BYTES);
+      if (kidx < n_tiles - 1) {
+        step(ck, 1);
+        ++kidx;
+      }
+      if (s >= 2 && vidx < n_tiles - 1) {
+        step(cv, 2);
+        ++vidx;
+      }
+    };
+    auto kbuf = [&](int slot) { return lds + (slot % kBufs) * SC::SLOT_BYTES; };
+    auto vbuf = [&](int slot) { return lds + (slot % kBufs) * SC::SLOT_BYTES + SC::TILE_BYTES; };
+
+    // ---- LDS read bases (see the main kernel): K fragment of k-step ks at
+    // kA ^ (32 ks), V^T fragment of output block db at vA ^ (64 db).
+    const int kA = k_off<D>(l32, hf);
+    int vA;
+    {
+      const int g4 = lane >> 4;
+      const int tr_t = (lane >> 2) & 3;
+      const int tr_s = lane & 3;
+      const int key0 = 4 * (g4 >> 1) + tr_t;
+      vA = v_off<D>(key0, 2 * (g4 & 1) + (tr_s >> 1)) + (tr_s & 1) * 8;
+    }
+
+    f32x16 s_cur[2], s_nxt[2];
+    bf16x2 p_prev[16], p_cur[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) p_prev[q] = bf16x2{(__bf16)0.0f, (__bf16)0.0f};
+
+    auto qk_products = [&](const char* kl, f32x16 (&sn)[2]) {
+      const int ka = opaque(kA);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const char* kp = kl + (ka ^ (32 * ks));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = *(const bf16x8*)(kp + kb * 32 * ROWB);
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : sn[kb], 0, 0, 0);
+        }
+      }
+    };
+    auto pv_products = [&](const char* vl, const bf16x2 (&pp)[16]) {
+      const int va = opaque(vA);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+          const int q0 = 8 * kb + 4 * tp;
+          const bf16x4 p_lo = __builtin_shufflevector(pp[q0], pp[q0 + 1], 0, 1, 2, 3);
+          const bf16x4 p_hi = __builtin_shufflevector(pp[q0 + 2], pp[q0 + 3], 0, 1, 2, 3);
+          const bf16x8 pf = __builtin_shufflevector(p_lo, p_hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const char* vp = vl + (va ^ (64 * db)) + (32 * kb + 16 * tp) * ROWB;
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
+            const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+          }
+        }
+    };
+
+    // ---- prologue: slots 0 .. kBufs-1; wait for slots 0 and 1; S_0
+    for (int s = 0; s < kBufs; ++s) copy_slot(s);
+    wait_vm<(kBufs - 2) * 2 * DPW>();
+    wg_barrier();
+    qk_products(kbuf(0), s_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    wg_barrier();  // buffer 0 is refilled by block 0
+
+    Cur cs{0, 0, 0, 0, nullptr};  // tile t (softmax, mask)
+    seek(cs, 0);
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    const int wrow0 = 32 * wave;      // this wave's first row, relative to the workgroup
+    const int myrow = wrow0 + l32;    // this lane's row, relative to the workgroup
+    for (int t = 0; t < n_tiles; ++t) {
+      copy_slot(t + kBufs);
+      __builtin_amdgcn_sched_barrier(0);
+      // mask keys past the block end and (causal) keys after this lane's row:
+      // key k of the tile is live iff k < thr
+      if (cs.t == ragged_t || (a.causal && cs.rel + (BN - 1) > wrow0)) {
+        int lim = cs.t == ragged_t ? kv_len - cs.t * BN : BN;
+        if (a.causal) {
+          const int lc = myrow - cs.rel + 1;
+          lim = lc < lim ? lc : lim;
+        }
+        const int thr = (lim < 0 ? 0 : lim) - 4 * hf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kb + 8 * (i >> 2) + (i & 3) >= thr) s_cur[kb][i] = -INFINITY;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // interleaved: P.V of tile t-1, S of tile t+1, softmax of tile t
+      const float mref = m2 == -INFINITY ? 0.f : m2;
+      pv_products(vbuf(t + 1), p_prev);
+      qk_products(kbuf(t + 1), s_nxt);
+      float rsq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int e = 2 * q;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][e & 15], c2s, -mref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][(e & 15) + 1], c2s, -mref));
+        p_cur[q] = bf16x2{(__bf16)p0, (__bf16)p1};
+        rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p_cur[q], ones, rsq[q & 3], false);
+      }
+      float rs = (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
+#if RA_SP_SCHED == 2
+      __builtin_amdgcn_iglp_opt(2);
+#elif RA_SP_SCHED == 3
+      __builtin_amdgcn_iglp_opt(3);
+#endif
+      __builtin_amdgcn_sched_barrier(0);
+      // move the reference when the tile's sums overflow the bound, or the
+      // row has none yet (see softmax_step)
+      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) {
+        float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
+#pragma unroll
+        for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s_cur[0][i]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[1][i]);
+        mx = pair_max(mx);
+        const float m_new = fmaxf(m2, mx * c2s);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
+        m2 = m_new;
+        rsq[0] = rsq[1] = rsq[2] = rsq[3] = 0.f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int e = 2 * q;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][e & 15], c2s, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][(e & 15) + 1], c2s, -m_use));
+          p_cur[q] = bf16x2{(__bf16)p0, (__bf16)p1};
+          rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p_cur[q], ones, rsq[q & 3], false);
+        }
+        rs = (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
+        lpart *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+      lpart += rs;
+      // slot t+2 (read by block t+1) has landed; kBufs-2 newer slots may fly
+      wait_vm<(kBufs - 2) * 2 * DPW>();
+      wg_barrier();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) p_prev[q] = p_cur[q];
+      step(cs, 0);
+    }
+    // P.V of the last tile (slot n+1 holds V_{n-1})
+    pv_products(vbuf(n_tiles + 1), p_prev);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<0>();
+  }
+
+  // ---- epilogue (as in the main kernel)
+  const float lsum = pair_sum(lpart);
+  if (!row_ok) return;
+  if (MODE == kInitStore || MODE == kLoadStore) {
+    if (hf == 0) {
+      a.m[sidx] = m2 * kLn2;
+      a.l[sidx] = lsum;
+    }
+    float* ap = a.acc + sidx * D + 4 * hf;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v4 = {acc[db][4 * g + 0], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+        *(f32x4*)(ap + 32 * db + 8 * g) = v4;
+      }
+  } else {
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    if (hf == 0) a.lse[sidx] = lsum > 0.f ? m2 * kLn2 + logf(lsum) : -INFINITY;
+    OutT* op = (OutT*)a.o + b * a.o_sb + r * a.o_ss + h * a.o_sh + 4 * hf;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        if constexpr (sizeof(OutT) == 2) {
+          bf16x4 o4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o4[j] = (__bf16)(acc[db][4 * g + j] * inv);
+          *(bf16x4*)(op + 32 * db + 8 * g) = o4;
+        } else {
+          f32x4 o4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o4[j] = acc[db][4 * g + j] * inv;
+          *(f32x4*)(op + 32 * db + 8 * g) = o4;
+        }
+      }
+  }
+}
+
+#ifndef RA_KERNEL
+#define RA_KERNEL 1  // 0: one tile at a time, 4 waves; 1: software-pipelined, 8 waves
+#endif
+
 template <int D, typename OutT, int MODE>
 hipError_t launch_t(const AttnArgs& a, const BlockTable& t, hipStream_t s) {
-  using C = Cfg<D>;
-  const int64_t n_qt = (a.q_len + BM - 1) / BM;
+  const int bm = RA_KERNEL ? BMS : BM;
+  const int nthreads = RA_KERNEL ? kSPThreads : kThreads;
+  const int64_t n_qt = (a.q_len + bm - 1) / bm;
   const int64_t n_work = (int64_t)a.batch * a.heads * n_qt;
   if (n_work == 0) return hipSuccess;
   const int64_t per = (n_work + 7) / 8;
-  auto kern = attn_bf16_kernel<D, OutT, MODE>;
+  auto kern = RA_KERNEL ? attn_bf16_sp_kernel<D, OutT, MODE> : attn_bf16_kernel<D, OutT, MODE>;
+  const int lds_bytes = RA_KERNEL ? SpCfg<D>::LDS_BYTES : Cfg<D>::LDS_BYTES;
   static bool attr_done = false;  // set once per instantiation; the attribute is idempotent
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(per * 8)), dim3(kThreads), C::LDS_BYTES, s, a, t);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per * 8)), dim3(nthreads), lds_bytes, s, a, t);
   return hipGetLastError();
 }
 

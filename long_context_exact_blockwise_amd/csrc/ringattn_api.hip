@@ -65,6 +65,9 @@ ra_status check_desc(const ra_desc* d) {
                     (long long)sts[t][i]);
     }
   }
+  // The kernels count keys of a block and tiles with 32-bit integers.
+  if (d->kv_len >= ((int64_t)1 << 30))
+    return fail(RA_E_UNSUPPORTED, "kv_len (%lld) must be below 2^30", (long long)d->kv_len);
   // The kernels address one 64-key tile of a block with 32-bit byte offsets.
   if (d->kv_stride[1] * esize(d->in_dtype) * 64 >= (int64_t)1 << 31)
     return fail(RA_E_UNSUPPORTED, "kv_stride[1] too large (a 64-key tile must span < 2 GiB)");

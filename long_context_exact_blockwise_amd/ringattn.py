@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libringattn.so")
+# RINGATTN_LIBRARY may name another build of the same library (same ABI).
+LIB_PATH = os.environ.get("RINGATTN_LIBRARY") or os.path.join(_HERE, "libringattn.so")
 
 RA_OK, RA_E_NULL, RA_E_SHAPE, RA_E_DTYPE, RA_E_ALIGN, RA_E_UNSUPPORTED, RA_E_MEMTYPE, RA_E_HIP = range(8)
 RA_F32, RA_BF16 = 0, 1
