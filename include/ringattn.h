@@ -93,7 +93,7 @@ typedef struct ra_desc {
   int32_t out_dtype;   /* ra_dtype of O                                       */
   int32_t flags;       /* RA_FLAG_*                                           */
   int64_t q_stride[3]; /* element strides of Q along (b, s, h)                */
-  int64_t kv_stride[3];/* element strides of every K and V block              */
+  int64_t kv_stride[3];/* element strides of every K and V block; (s) >= D   */
   int64_t o_stride[3]; /* element strides of O                                */
 } ra_desc;
 

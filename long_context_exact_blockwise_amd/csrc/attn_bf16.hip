@@ -1,9 +1,9 @@
 // bf16 blockwise attention with online-softmax merge, gfx950 (MI355X).
 //
-// One workgroup owns BM = 128 query rows of one (batch, head) and streams the
-// KV blocks it is given, tile by tile (BN = 64 keys), through LDS.  The state
-// of the online softmax (running max m, running sum l, unnormalised output
-// acc; the triple of the "Gotchas and Failure Modes" section of "Ring
+// One workgroup (8 waves) owns BM = 256 query rows of one (batch, head) and
+// streams the KV blocks it is given, tile by tile (BN = 64 keys), through LDS.
+// The state of the online softmax (reference m, running sum l, unnormalised
+// output acc; the triple of the "Gotchas and Failure Modes" section of "Ring
 // Attention: Train 1M Tokens on 8GB GPUs in 2026") lives in registers for the
 // whole launch, so a fused launch over all ring blocks never round-trips it
 // through HBM.
@@ -12,15 +12,23 @@
 //   S^T[64 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16_bf16, K from LDS,
 //                                         Q fragments held in registers
 //   causal / ragged mask (diagonal and tail tiles only)
-//   m' = max(m, rowmax S); p = exp2(S*c - m'); l = l*2^(m-m') + sum p;
-//   acc *= 2^(m-m') (skipped when no row's max moved)      c = scale*log2(e)
+//   p = exp2(S*c - m); l += sum p         c = scale*log2(e), m a reference
+//                                         point (see softmax_redo)
 //   O^T[D x 32 rows] += V^T . P^T         v_mfma_f32_32x32x16_bf16, V^T gathered
 //                                         from LDS with ds_read_b64_tr_b16
 // Computing S transposed puts one query row in each lane column of the MFMA
-// result, so row max / row sum are per-lane scalars (plus one swap between
-// the two 32-lane halves) and the S^T result registers are directly the P^T
-// operand of the second product once the keys inside each 16-key step are
-// permuted the same way on the V side.
+// result, so row sums are per-lane scalars (plus one swap between the two
+// 32-lane halves) and the S^T result registers are directly the P^T operand
+// of the second product once the keys inside each 16-key step are permuted
+// the same way on the V side.
+//
+// Software pipeline: a wave's work on tile t is a chain (S_t, softmax of S_t,
+// P_t V_t), so run in order the matrix cores idle during the softmax.  Block t
+// of the main loop instead issues three independent pieces of work, which the
+// scheduler interleaves instruction by instruction:
+//   O^T += V_{t-1}^T P_{t-1}^T   (P from the previous block)
+//   S_{t+1}^T = K_{t+1} Q^T
+//   softmax of S_t -> P_t        (vector ALU: exp2, bf16 pack, row sums)
 #include <type_traits>
 
 #include "ra_internal.h"
@@ -33,31 +41,53 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BM = 32 * kWaves;  // query rows per workgroup
 constexpr int BN = 64;           // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// K/V slots in LDS: slot s = (K_s, V_{s-2}) lives in buffer s % kBufs and is
+// read in block s-1.  Block t copies slot t + kBufs into the buffer of slot t
+// (read in block t-1) and waits for slot t+2 before the barrier that ends it,
+// so kBufs-2 slots stay in flight across barriers.  Slots past the last tile
+// (and the V part of slots 0, 1) copy a real tile whose products are
+// discarded or multiplied by P = 0: every block issues the same number of
+// copies and the wait counts stay exact.
+#ifndef RA_SP_BUFS
+#define RA_SP_BUFS 4
+#endif
+constexpr int kBufs = RA_SP_BUFS;
+
 template <int D>
 struct Cfg {
-  static constexpr int CH = D / 8;                       // 16-byte chunks per K/V row
-  static constexpr int DMA_PER_WAVE = BN * D * 2 / 1024 / kWaves;  // 1 KiB LDS-DMA copies per wave per tile
-  static constexpr int KS = D / 16;                      // k-steps of Q.K^T
-  static constexpr int DB = D / 32;                      // 32-row blocks of O^T
+  static constexpr int CH = D / 8;   // 16-byte chunks per K/V row
+  static constexpr int KS = D / 16;  // k-steps of Q.K^T
+  static constexpr int DB = D / 32;  // 32-row blocks of O^T
   static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;       // K and V, double-buffered
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
+  static constexpr int LDS_BYTES = kBufs * SLOT_BYTES;
+  static constexpr int DPW = TILE_BYTES / 1024 / kWaves;  // 1 KiB copies per wave per K (or V) tile
+  // In a slot, wave w's K chunks w*DPW + j and V chunks w*DPW + j sit
+  // together (K first) in a 2*DPW KiB region: byte lin of the row-major
+  // (swizzled) K or V tile maps to these slot offsets.  A linear offset that
+  // is a multiple of DPW KiB maps to twice itself.
+  static __device__ __forceinline__ int k_at(int lin) {
+    const int blk = lin >> 10;
+    return (blk / DPW) * (2 * DPW * 1024) + (blk % DPW) * 1024 + (lin & 1023);
+  }
+  static __device__ __forceinline__ int v_at(int lin) { return k_at(lin) + DPW * 1024; }
 };
 
-// LDS placement of 16-byte chunk c of key row `key`.  K rows are read 16 bytes
-// per lane, 16 rows at a time at one chunk column: XOR the column with the row
-// so those 16 reads hit 16 different 16-byte bank groups.  V rows are read by
-// the transpose loads 8 rows x 4 chunks at a time: XOR the 4-chunk group with
-// the row so the 8 rows spread over the banks.
+// Row-major placement of 16-byte chunk c of key row `key` in a tile.  K rows
+// are read 16 bytes per lane, 16 rows at a time at one chunk column: XOR the
+// column with the row so those 16 reads hit 16 different 16-byte bank groups.
+// V rows are read by the transpose loads 8 rows x 4 chunks at a time: XOR the
+// 4-chunk group with the row so the 8 rows spread over the banks.
 template <int D>
 __device__ __forceinline__ int k_off(int key, int c) {
   const int cs = (D == 128) ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7));
@@ -79,79 +109,67 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Hide a value from loop-invariant code motion: the compiler must recompute
-// whatever is derived from the result where it is used, instead of keeping
-// every derived address live in registers across the loop.
-__device__ __forceinline__ int opaque(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 // Row-sum bound of one tile under a stale reference: while every p of the
 // tile stays <= 2^12 the reference may lag the running max.
 constexpr float kPLim = 4096.0f;
 
-// One online-softmax step for the 32 raw scores q.k (two f32x16 fragments of
-// S^T) this lane holds for its query row; the other 32 keys of the tile sit in
-// the lane 32 away, which holds the same row.
-//
+// Exponentiate the 32 raw scores q.k (two f32x16 fragments of S^T) this lane
+// holds for its query row against reference mref (log2 units): bf16 pairs
+// p[q] = (p_{2q}, p_{2q+1}) for the P.V product; returns their sum (of the
+// same bf16 values).  The other 32 keys of the tile sit in the lane 32 away.
+__device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c2, float mref, bf16x2 (&p)[16]) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float rsq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = 2 * q;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c2, -mref));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][(e & 15) + 1], c2, -mref));
+    p[q] = bf16x2{(__bf16)p0, (__bf16)p1};
+    rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p[q], ones, rsq[q & 3], false);
+  }
+  return (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
+}
+
 // The state is (m2, l, acc) with m2 a reference point in log2 units: l and acc
 // are sums of exp2(s*c - m2).  Any m2 gives the same acc/l and m2 + log2 l, so
-// m2 is moved only when it must be: the tile is first exponentiated against
-// the current m2, and only if some lane of the wave then sees a row sum above
-// kPLim (the max has grown by more than 12 in log2 units, or overflowed), or
-// still has no reference (m2 = -inf), is m2 raised to the running max, the
-// tile exponentiated again and acc, l rescaled.  m2 never exceeds the running
-// max (it is only ever set to it), so l >= 1 once a key was seen.
-//
-// Writes the bf16 pairs p[q] = (p_{2q}, p_{2q+1}) that the P.V product uses
-// and adds their sum (of the same bf16 values) to lpart.
+// m2 is moved only when it must be: a tile is first exponentiated against the
+// current m2 (softmax_exp), and only if some lane of the wave then sees a row
+// sum above kPLim (the max has grown by more than 12 in log2 units, or
+// overflowed), or still has no reference (m2 = -inf), does softmax_redo raise
+// m2 to the running max, exponentiate the tile again and rescale acc and l.
+// m2 never exceeds the running max (it is only ever set to it), so l >= 1
+// once a key was seen.  Returns the tile's row sum against the final m2.
 template <int DB>
-__device__ __forceinline__ void softmax_step(const f32x16 (&s)[2], float c2, float& m2, float& lpart,
-                                             f32x16 (&acc)[DB], bf16x2 (&p)[16]) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  auto expo = [&](float mref) -> float {
-    float rsq[4] = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ float softmax_redo(const f32x16 (&s)[2], float c2, float& m2, float& lpart,
+                                              f32x16 (&acc)[DB], bf16x2 (&p)[16]) {
+  float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int e = 2 * q;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c2, -mref));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][(e & 15) + 1], c2, -mref));
-      p[q] = bf16x2{(__bf16)p0, (__bf16)p1};
-      rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p[q], ones, rsq[q & 3], false);
-    }
-    return (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
-  };
-  float rs = expo(m2 == -INFINITY ? 0.f : m2);
-  if (__any(!(rs <= kPLim) || m2 == -INFINITY)) {
-    float mx = fmaxf(s[0][0], s[0][1]);
+  for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-    for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+  for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+  mx = pair_max(mx);
+  const float m_new = fmaxf(m2, mx * c2);
+  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
+  m2 = m_new;
+  lpart *= alpha;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-    mx = pair_max(mx);
-    const float m_new = fmaxf(m2, mx * c2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
-    m2 = m_new;
-    rs = expo(m_use);
-    lpart *= alpha;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-  }
-  lpart += rs;
+    for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+  return softmax_exp(s, c2, m_use, p);
 }
 
 // Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
-// i's bytes land at lds_dst + 16 i.  base and lds_dst are wave-uniform.  The
-// copy is issued from inline assembly so that the compiler does not track it:
-// its own tracking would wait for every copy in flight before the next LDS
-// read of any buffer, which serialises the prefetch with the compute.  The
-// kernels wait for their copies themselves (s_waitcnt vmcnt) before the
-// barrier that publishes a buffer.
+// i's bytes land at LDS byte lds_addr + 16 i.  base and lds_addr are
+// wave-uniform.  The copies are issued from inline assembly so that the
+// compiler does not track them: its own tracking would wait for every copy in
+// flight before the next LDS read of any buffer, which serialises the prefetch
+// with the compute.  The kernel waits for its copies itself (s_waitcnt
+// vmcnt) before the barrier that publishes a buffer.
 __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
+  // (readfirstlane returns int: widen through uint32_t, never by sign extension)
   const uint64_t bv = (uint64_t)base;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
@@ -167,6 +185,53 @@ __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint3
       : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
+
+// A wave's share of one K/V slot with a single M0 value: DPW 1 KiB chunks of
+// K at m0 + 1 KiB j and DPW chunks of V at m0 + 1 KiB (DPW + j).  The
+// instruction offset moves the LDS destination and the global address alike,
+// so lane offsets are passed with that offset taken out (ko_j = K offset -
+// 1 KiB j) and the V base is passed 1 KiB DPW low.  Changing M0 while copies
+// are in flight stalls the wave, so it is set once per slot.
+template <int DPW>
+__device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbase_low, const uint32_t (&ko)[DPW],
+                                             const uint32_t (&vo)[DPW], uint32_t m0) {
+  const uint64_t kb = (uint64_t)kbase, vb = (uint64_t)vbase_low;
+  const uint32_t klo = __builtin_amdgcn_readfirstlane((uint32_t)kb);
+  const uint32_t khi = __builtin_amdgcn_readfirstlane((uint32_t)(kb >> 32));
+  const uint32_t vlo = __builtin_amdgcn_readfirstlane((uint32_t)vb);
+  const uint32_t vhi = __builtin_amdgcn_readfirstlane((uint32_t)(vb >> 32));
+  const uint64_t kbs = ((uint64_t)khi << 32) | klo;
+  const uint64_t vbs = ((uint64_t)vhi << 32) | vlo;
+  uint32_t saved;
+  if constexpr (DPW == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %5\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %6\n\t"
+        "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
+        "global_load_lds_dwordx4 %3, %7 offset:2048\n\t"
+        "global_load_lds_dwordx4 %4, %7 offset:3072\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(ko[0]), "v"(ko[1]), "v"(vo[0]), "v"(vo[1]), "s"(__builtin_amdgcn_readfirstlane(m0)), "s"(kbs),
+          "s"(vbs)
+        : "memory");
+  } else {
+    static_assert(DPW == 1, "one or two chunks per wave");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %4\n\t"
+        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(ko[0]), "v"(vo[0]), "s"(__builtin_amdgcn_readfirstlane(m0)), "s"(kbs), "s"(vbs)
+        : "memory");
+  }
+}
+
 // LDS byte address of a generic pointer into the dynamic LDS array.
 __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -205,6 +270,8 @@ template <int D, typename OutT, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, BlockTable tbl) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int ROWB = D * 2;
+  constexpr int DPW = C::DPW;
 
   const int n_qt = (int)((a.q_len + BM - 1) / BM);
   const int n_work = a.batch * a.heads * n_qt;
@@ -220,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
   const int h = bh - b * a.heads;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
@@ -231,9 +298,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
   RowRange rr;
   rr.first_pos = a.q_pos0 + row0;
   rr.last_pos = a.q_pos0 + ((row0 + BM < a.q_len) ? row0 + BM : a.q_len) - 1;
-  const int64_t wave_last_pos = a.q_pos0 + row0 + 32 * wave + 31;
-  const int64_t my_pos = a.q_pos0 + r;
-  const float c2 = a.scale * kLog2e;
+  const float c2s = a.scale * kLog2e;
+  const int kv_len = (int)a.kv_len;  // < 2^30 (checked on the host)
+
+  int n_tiles = 0;
+  for (int bi = 0; bi < a.nblocks; ++bi) n_tiles += block_tiles(a, tbl.pos0[bi], rr);
+  // A per-block launch (state in HBM) whose rows see no key of the block
+  // leaves the state untouched.
+  if (MODE == kLoadStore && n_tiles == 0) return;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds row r, d = 16ks + 8hf + 0..7
   bf16x8 qf[C::KS];
@@ -249,347 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
       }
     }
   }
-
-  // ---- state: m2 (running max in log2 units), l (this lane's half of the sum), acc
-  const int64_t sidx = ((int64_t)b * a.heads + h) * a.q_len + r;
-  float m2 = -INFINITY;
-  float lpart = 0.f;
-  f32x16 acc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
-  // ---- tile loader: direct global -> LDS copies (global_load_lds_dwordx4).
-  // One instruction moves 64 lanes x 16 bytes into 1 KiB of LDS at M0, lane i
-  // filling bytes [16i, 16i+16).  Each lane therefore fetches the global chunk
-  // that the swizzled layout wants in its LDS slot.  The per-lane byte offsets
-  // inside a tile are loop-invariant; only keys past the end of a block (the
-  // ragged last tile) are clamped onto the block's last key: their scores are
-  // masked to -inf, so their values meet an exact 0 and only need to be finite.
-  uint32_t dk[C::DMA_PER_WAVE], dv[C::DMA_PER_WAVE];
-#pragma unroll
-  for (int j = 0; j < C::DMA_PER_WAVE; ++j) {
-    const int slot = (wave * C::DMA_PER_WAVE + j) * 64 + lane;
-    const int key = slot / C::CH;
-    const int cs = slot % C::CH;
-    const int ck = k_off<D>(key, cs) / 16 - key * C::CH;  // the XOR swizzle is its own inverse
-    const int cv = v_off<D>(key, cs) / 16 - key * C::CH;
-    dk[j] = (uint32_t)(key * a.kv_ss * 2 + ck * 16);
-    dv[j] = (uint32_t)(key * a.kv_ss * 2 + cv * 16);
-  }
-  const int64_t kv_head_off = ((int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh) * 2;
-  auto issue_tile = [&](int bi, int t, int buf) {
-    const int64_t t0 = (int64_t)t * BN;
-    const char* kt = (const char*)tbl.k[bi] + kv_head_off + t0 * a.kv_ss * 2;
-    const char* vt = (const char*)tbl.v[bi] + kv_head_off + t0 * a.kv_ss * 2;
-    char* kl = lds + buf * C::TILE_BYTES;
-    char* vl = lds + (2 + buf) * C::TILE_BYTES;
-    const bool ragged = t0 + BN > a.kv_len;
-#pragma unroll
-    for (int j = 0; j < C::DMA_PER_WAVE; ++j) {
-      const int blk = wave * C::DMA_PER_WAVE + j;
-      uint32_t ok = dk[j], ov = dv[j];
-      if (ragged) {
-        const int slot = blk * 64 + lane;
-        const int key = slot / C::CH;
-        const int last = (int)(a.kv_len - 1 - t0);
-        const int kc = key < last ? key : last;
-        const uint32_t shift = (uint32_t)((key - kc) * a.kv_ss * 2);
-        ok -= shift;
-        ov -= shift;
-      }
-      lds_dma16(kt, ok, lds_addr_of(kl) + blk * 1024);
-      lds_dma16(vt, ov, lds_addr_of(vl) + blk * 1024);
-    }
-  };
-  // Tile cursor over the blocks in order: block b, tile t of n visible tiles.
-  struct Cur {
-    int b, t, n;
-  };
-  auto seek = [&](Cur& c) -> bool {  // first visible tile at or after block c.b
-    while (c.b < a.nblocks && (c.n = block_tiles(a, tbl.pos0[c.b], rr)) == 0) ++c.b;
-    c.t = 0;
-    return c.b < a.nblocks;
-  };
-  auto step = [&](Cur& c) -> bool {
-    if (++c.t < c.n) return true;
-    ++c.b;
-    return seek(c);
-  };
-
-  // ---- per-lane LDS read bases.  K: row l32 (+32 per key block, an immediate),
-  // chunk 2ks+hf.  V^T via transpose loads: in each 16-lane group g, lane
-  // 4t+s addresses key row t of a 4-row group and columns 4s..4s+3 of a
-  // 16-column slice; it receives column (lane & 15) of those 4 rows.  Rows
-  // 4*(g>>1) + t (+8 for the second load, +16 per key step, +32 per key
-  // block: immediates), columns 32db + 16*(g&1) + 4s.
-  int kbase[C::KS];
-#pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) kbase[ks] = k_off<D>(l32, 2 * ks + hf);
-  int vbase[C::DB];
-  {
-    const int grp = lane >> 4;
-    const int tr_t = (lane >> 2) & 3;
-    const int tr_s = lane & 3;
-    const int key0 = 4 * (grp >> 1) + tr_t;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-      vbase[db] = v_off<D>(key0, 4 * db + 2 * (grp & 1) + (tr_s >> 1)) + (tr_s & 1) * 8;
-  }
-  constexpr int ROWB = D * 2;  // bytes per key row in LDS
-
-  const int64_t wave_first_pos = a.q_pos0 + row0 + 32 * wave;
-  Cur cur{0, 0, 0};
-  bool have = seek(cur);
-  // A per-block launch (state in HBM) whose rows see no key of the block
-  // leaves the state untouched.
-  if (MODE == kLoadStore && !have) return;
-  if (MODE == kLoadStore || MODE == kLoadFinalize) {
-    if (row_ok) {
-      m2 = a.m[sidx] * kLog2e;
-      lpart = hf == 0 ? a.l[sidx] : 0.f;
-      const float* ap = a.acc + sidx * D + 4 * hf;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v4 = *(const f32x4*)(ap + 32 * db + 8 * g);
-          acc[db][4 * g + 0] = v4[0];
-          acc[db][4 * g + 1] = v4[1];
-          acc[db][4 * g + 2] = v4[2];
-          acc[db][4 * g + 3] = v4[3];
-        }
-    }
-  }
-
-  if (have) issue_tile(cur.b, cur.t, 0);
-  wait_vm<0>();
-  __syncthreads();
-  int buf = 0;
-  while (have) {
-    Cur nxt = cur;
-    const bool have_next = step(nxt);
-    if (have_next) issue_tile(nxt.b, nxt.t, buf ^ 1);
-    const int bi = cur.b, t = cur.t;
-
-    const int64_t t0 = (int64_t)t * BN;
-    const int64_t tile_pos = tbl.pos0[bi] + t0;  // global position of the tile's key 0
-    const bool wave_skip = a.causal && tile_pos > wave_last_pos;
-    if (!wave_skip) {
-      const char* kl = lds + buf * C::TILE_BYTES;
-      const char* vl = lds + (2 + buf) * C::TILE_BYTES;
-      // S^T = K Q^T.  K fragments are read two k-steps ahead of their
-      // products (the group barriers pin that order).
-      f32x16 s[2];
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *(const bf16x8*)(kl + kbase[ks] + kb * 32 * ROWB);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int st = 0; st < 2 * C::KS - 4; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // mask keys past the block end and (causal) keys after this lane's row:
-      // key k of the tile is live iff k < thr.
-      const bool need_mask = (t0 + BN > a.kv_len) || (a.causal && tile_pos + BN - 1 > wave_first_pos);
-      if (need_mask) {
-        int64_t lim = a.kv_len - t0;
-        if (a.causal) {
-          const int64_t lc = my_pos - tile_pos + 1;
-          lim = lc < lim ? lc : lim;
-        }
-        const int thr = (int)(lim < 0 ? 0 : (lim > BN ? BN : lim)) - 4 * hf;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kb + 8 * (i >> 2) + (i & 3);
-            if (key >= thr) s[kb][i] = -INFINITY;
-          }
-      }
-      bf16x2 pp[16];
-      softmax_step<C::DB>(s, c2, m2, lpart, acc, pp);
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-          const int q0 = 8 * kb + 4 * tp;
-          const bf16x4 p_lo = __builtin_shufflevector(pp[q0], pp[q0 + 1], 0, 1, 2, 3);
-          const bf16x4 p_hi = __builtin_shufflevector(pp[q0 + 2], pp[q0 + 3], 0, 1, 2, 3);
-          pf[kb][tp] = __builtin_shufflevector(p_lo, p_hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int tp = 0; tp < 2; ++tp) {
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const char* vp = vl + vbase[db] + (32 * kb + 16 * tp) * ROWB;
-            // (Assembled with a shuffle of two bf16x4 loads: building the
-            // fragment element by element from bit-cast 16-bit integers is
-            // miscompiled by this toolchain, which drops half the elements.)
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-            const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][tp], acc[db], 0, 0, 0);
-          }
-        }
-      // V fragments two products ahead of their MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int st = 0; st < 4 * C::DB - 2; ++st) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-
-    wait_vm<0>();
-    __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    have = have_next;
-  }
-
-  // ---- epilogue
-  const float lsum = pair_sum(lpart);
-  if (!row_ok) return;
-  if (MODE == kInitStore || MODE == kLoadStore) {
-    if (hf == 0) {
-      a.m[sidx] = m2 * kLn2;
-      a.l[sidx] = lsum;
-    }
-    float* ap = a.acc + sidx * D + 4 * hf;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v4 = {acc[db][4 * g + 0], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
-        *(f32x4*)(ap + 32 * db + 8 * g) = v4;
-      }
-  } else {
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    if (hf == 0) a.lse[sidx] = lsum > 0.f ? m2 * kLn2 + logf(lsum) : -INFINITY;
-    OutT* op = (OutT*)a.o + b * a.o_sb + r * a.o_ss + h * a.o_sh + 4 * hf;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        if constexpr (sizeof(OutT) == 2) {
-          bf16x4 o4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o4[j] = (__bf16)(acc[db][4 * g + j] * inv);
-          *(bf16x4*)(op + 32 * db + 8 * g) = o4;
-        } else {
-          f32x4 o4;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o4[j] = acc[db][4 * g + j] * inv;
-          *(f32x4*)(op + 32 * db + 8 * g) = o4;
-        }
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Software-pipelined variant: 8 waves, 256 query rows per workgroup, K/V tiles
-// shared by all eight waves.
-//
-// A wave's work on tile t is a chain: S_t = K_t Q^T, then the softmax of S_t,
-// then O += V_t P_t.  Run in that order, the matrix cores idle during the
-// softmax.  Here block t of the loop issues, interleaved instruction by
-// instruction, three independent pieces of work:
-//   O^T += V_{t-1}^T P_{t-1}^T   (16 MFMAs, P from the previous block)
-//   S_{t+1}^T = K_{t+1} Q^T      (16 MFMAs)
-//   softmax of S_t -> P_t        (vector ALU: exp2, bf16 pack, row sums)
-// so the softmax runs under the matrix products.  The (rare) move of the
-// softmax reference, with its rescale of acc, follows the interleaved part.
-//
-// LDS holds kBufs slots; slot s = (K_s, V_{s-2}) lives in buffer s % kBufs and
-// is read in block s-1.  Block t copies slot t + kBufs into the buffer of
-// slot t (read in block t-1) with direct global->LDS loads, each wave a
-// share, and waits for slot t+2 before the barrier that ends it: kBufs-2
-// slots stay in flight across barriers.  Slots past the last tile (and the V
-// part of slots 0, 1) copy a real tile whose products are discarded or
-// multiplied by P = 0, so every block issues the same number of copies and
-// the wait counts stay exact.
-constexpr int kSPWaves = 8;
-constexpr int kSPThreads = 64 * kSPWaves;
-constexpr int BMS = 32 * kSPWaves;  // query rows per workgroup
-#ifndef RA_SP_BUFS
-#define RA_SP_BUFS 4
-#endif
-constexpr int kBufs = RA_SP_BUFS;
-#ifndef RA_SP_SCHED
-#define RA_SP_SCHED 3  // interleave of the block's matrix products with its softmax: 0 compiler, 2/3 iglp strategies
-#endif
-
-template <int D>
-struct SpCfg {
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
-  static constexpr int LDS_BYTES = kBufs * SLOT_BYTES;
-  static constexpr int DPW = TILE_BYTES / 1024 / kSPWaves;  // 1 KiB copies per wave per K (or V) tile
-};
-
-template <int D, typename OutT, int MODE>
-__global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a, BlockTable tbl) {
-  using C = Cfg<D>;
-  using SC = SpCfg<D>;
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  constexpr int ROWB = D * 2;
-  constexpr int DPW = SC::DPW;
-
-  const int n_qt = (int)((a.q_len + BMS - 1) / BMS);
-  const int n_work = a.batch * a.heads * n_qt;
-  const int per = (n_work + 7) >> 3;
-  const int wid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (wid >= n_work) return;
-  const int bh = wid / n_qt;
-  const int qt = n_qt - 1 - (wid - bh * n_qt);
-  const int b = bh / a.heads;
-  const int h = bh - b * a.heads;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
-  const int lane = tid & 63;
-  const int l32 = lane & 31;
-  const int hf = lane >> 5;
-
-  const int64_t row0 = (int64_t)qt * BMS;
-  const int64_t r = row0 + 32 * wave + l32;
-  const bool row_ok = r < a.q_len;
-  RowRange rr;
-  rr.first_pos = a.q_pos0 + row0;
-  rr.last_pos = a.q_pos0 + ((row0 + BMS < a.q_len) ? row0 + BMS : a.q_len) - 1;
-  const float c2s = a.scale * kLog2e;
-  const int kv_len = (int)a.kv_len;  // < 2^30 (checked on the host)
-
-  int n_tiles = 0;
-  for (int bi = 0; bi < a.nblocks; ++bi) n_tiles += block_tiles(a, tbl.pos0[bi], rr);
-  if (MODE == kLoadStore && n_tiles == 0) return;  // leaves the state untouched
-
-  bf16x8 qf[C::KS];
-  {
-    const __bf16* qp = (const __bf16*)a.q + b * a.q_sb + r * a.q_ss + h * a.q_sh + 8 * hf;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      if (row_ok) {
-        qf[ks] = *(const bf16x8*)(qp + 16 * ks);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qf[ks][j] = (__bf16)0.0f;
-      }
-    }
-  }
+  // ---- state: m2 (reference, log2 units), l (this lane's half of the sum), acc
   const int64_t sidx = ((int64_t)b * a.heads + h) * a.q_len + r;
   float m2 = -INFINITY;
   float lpart = 0.f;
@@ -645,10 +377,12 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
     };
     // The ragged tile of a block (keys past kv_len) is its last one.
     const int ragged_t = (kv_len & (BN - 1)) ? (kv_len >> 6) : -1;
-    // Per-lane byte offsets of this wave's share of a tile: copy j moves
-    // 1 KiB = 64 lanes x 16 bytes into LDS chunk blk = wave*DPW + j; lane i
-    // fetches the global chunk that the swizzled layout puts at byte 16 i.
-    uint32_t dk[DPW], dv[DPW];
+
+    // ---- copies into LDS.  Copy j of a wave's K (or V) share moves 1 KiB =
+    // 64 lanes x 16 bytes: LDS chunk blk = wave*DPW + j of the row-major tile,
+    // lane i fetching the global chunk that the swizzled layout puts at byte
+    // 16 i of it.
+    uint32_t dk[DPW], dv[DPW], dkj[DPW], dvj[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int slot = (wave * DPW + j) * 64 + lane;
@@ -656,18 +390,22 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
       const int cs = slot % C::CH;
       dk[j] = (uint32_t)(key * a.kv_ss * 2 + (k_off<D>(key, cs) / 16 - key * C::CH) * 16);
       dv[j] = (uint32_t)(key * a.kv_ss * 2 + (v_off<D>(key, cs) / 16 - key * C::CH) * 16);
+      // chunk j's key rows start at >= 1 KiB j of the source (a row is >= D*2
+      // bytes), so taking the instruction offset out stays non-negative
+      dkj[j] = dk[j] - 1024u * j;
+      dvj[j] = dv[j] - 1024u * j;
     }
-    const uint32_t lds0 = lds_addr_of(lds) + wave * DPW * 1024;  // this wave's first chunk of a tile
-    auto copy_tile = [&](const Cur& c, bool is_v, uint32_t dst) {
+    const uint32_t lds_base = lds_addr_of(lds);
+    const uint32_t lds0 = lds_base + wave * (2 * DPW * 1024);  // this wave's region of a slot
+    // Ragged tile: keys past the block end re-read its last key (masked
+    // later); one chunk at a time with its own M0.
+    auto copy_ragged = [&](const Cur& c, bool is_v, uint32_t dst) {
 #pragma unroll
       for (int j = 0; j < DPW; ++j) {
-        uint32_t off = is_v ? dv[j] : dk[j];
-        if (c.t == ragged_t) {  // keys past the block end re-read its last key (masked later)
-          const int key = ((wave * DPW + j) * 64 + lane) / C::CH;
-          const int last = kv_len - 1 - c.t * BN;
-          off -= (uint32_t)((key > last ? key - last : 0) * a.kv_ss * 2);
-        }
-        lds_dma16(c.src, off, dst + j * 1024);
+        const int key = ((wave * DPW + j) * 64 + lane) / C::CH;
+        const int last = kv_len - 1 - c.t * BN;
+        const uint32_t off = (is_v ? dv[j] : dk[j]) - (uint32_t)((key > last ? key - last : 0) * a.kv_ss * 2);
+        lds_dma16(c.src, off, dst + (is_v ? DPW + j : j) * 1024);
       }
     };
     // copy cursors: K of slot s is tile min(s, n-1); V of slot s is tile
@@ -677,9 +415,13 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
     seek(cv, 2);
     int kidx = 0, vidx = 0;
     auto copy_slot = [&](int s) {
-      const uint32_t dst = lds0 + (uint32_t)((s % kBufs) * SC::SLOT_BYTES);
-      copy_tile(ck, false, dst);
-      copy_tile(cv, true, dst + SC::TILE_BYTES);
+      const uint32_t dst = lds0 + (uint32_t)((s % kBufs) * C::SLOT_BYTES);
+      if (ck.t != ragged_t && cv.t != ragged_t) {
+        lds_dma_slot<DPW>(ck.src, cv.src - DPW * 1024, dkj, dvj, dst);
+      } else {
+        copy_ragged(ck, false, dst);
+        copy_ragged(cv, true, dst);
+      }
       if (kidx < n_tiles - 1) {
         step(ck, 1);
         ++kidx;
@@ -689,40 +431,56 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
         ++vidx;
       }
     };
-    auto kbuf = [&](int slot) { return lds + (slot % kBufs) * SC::SLOT_BYTES; };
-    auto vbuf = [&](int slot) { return lds + (slot % kBufs) * SC::SLOT_BYTES + SC::TILE_BYTES; };
+    auto slot_at = [&](int s) -> uint32_t { return lds_base + (uint32_t)((s % kBufs) * C::SLOT_BYTES); };
 
-    // ---- LDS read bases (see the main kernel): K fragment of k-step ks at
-    // kA ^ (32 ks), V^T fragment of output block db at vA ^ (64 db).
-    const int kA = k_off<D>(l32, hf);
-    int vA;
+    // ---- per-lane LDS byte offsets inside a slot.  K: row l32 (+32 per key
+    // block), chunk 2ks+hf: kofs[ks].  V^T via transpose loads: in each
+    // 16-lane group g, lane 4t+s addresses key row t of a 4-row group and
+    // columns 4s..4s+3 of a 16-column slice; it receives column (lane & 15)
+    // of those 4 rows.  Rows 4*(g>>1) + t (+8 for the second load, +16 per
+    // key step, +32 per key block), columns 32db + 16*(g&1) + 4s: vofs[db].
+    // Row offsets are multiples of 8 rows (of DPW KiB), which the slot layout
+    // doubles; they are instruction immediates.
+    int kofs[C::KS], vofs[C::DB];
     {
+      const int kA = k_off<D>(l32, hf);
       const int g4 = lane >> 4;
       const int tr_t = (lane >> 2) & 3;
       const int tr_s = lane & 3;
       const int key0 = 4 * (g4 >> 1) + tr_t;
-      vA = v_off<D>(key0, 2 * (g4 & 1) + (tr_s >> 1)) + (tr_s & 1) * 8;
+      const int vA = v_off<D>(key0, 2 * (g4 & 1) + (tr_s >> 1)) + (tr_s & 1) * 8;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) kofs[ks] = C::k_at(kA ^ (32 * ks));
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) vofs[db] = C::v_at(vA ^ (64 * db));
     }
+    auto k_frag = [&](uint32_t sl, int ks, int kb) -> bf16x8 {
+      return *(lds_bf16x8*)(size_t)(sl + kofs[ks] + 2 * kb * 32 * ROWB);
+    };
+    auto v_frag = [&](uint32_t sl, int db, int row) -> bf16x8 {
+      const uint32_t va = sl + vofs[db] + 2 * row * ROWB;
+      // (Assembled with a shuffle of two bf16x4 loads: building the fragment
+      // element by element from bit-cast 16-bit integers is miscompiled by
+      // this toolchain, which drops half the elements.)
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)va);
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(va + 2 * 8 * ROWB));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 
-    f32x16 s_cur[2], s_nxt[2];
-    bf16x2 p_prev[16], p_cur[16];
+    f32x16 s_cur[2], s_nxt[2];     // S^T of tile t (softmax now) and t+1 (being computed)
+    bf16x2 p_prev[16], p_cur[16];  // P of tile t-1 (P.V now) and t (being produced)
 #pragma unroll
     for (int q = 0; q < 16; ++q) p_prev[q] = bf16x2{(__bf16)0.0f, (__bf16)0.0f};
 
-    auto qk_products = [&](const char* kl, f32x16 (&sn)[2]) {
-      const int ka = opaque(kA);
+    auto qk_products = [&](uint32_t sl, f32x16 (&sn)[2]) {
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const char* kp = kl + (ka ^ (32 * ks));
+      for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 kf = *(const bf16x8*)(kp + kb * 32 * ROWB);
-          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : sn[kb], 0, 0, 0);
-        }
-      }
+        for (int kb = 0; kb < 2; ++kb)
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(sl, ks, kb), qf[ks], ks == 0 ? f32x16{} : sn[kb],
+                                                           0, 0, 0);
     };
-    auto pv_products = [&](const char* vl, const bf16x2 (&pp)[16]) {
-      const int va = opaque(vA);
+    auto pv_products = [&](uint32_t sl, const bf16x2 (&pp)[16]) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -732,13 +490,8 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
           const bf16x4 p_hi = __builtin_shufflevector(pp[q0 + 2], pp[q0 + 3], 0, 1, 2, 3);
           const bf16x8 pf = __builtin_shufflevector(p_lo, p_hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const char* vp = vl + (va ^ (64 * db)) + (32 * kb + 16 * tp) * ROWB;
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * ROWB));
-            const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
-          }
+          for (int db = 0; db < C::DB; ++db)
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(sl, db, 32 * kb + 16 * tp), pf, acc[db], 0, 0, 0);
         }
     };
 
@@ -746,15 +499,14 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
     for (int s = 0; s < kBufs; ++s) copy_slot(s);
     wait_vm<(kBufs - 2) * 2 * DPW>();
     wg_barrier();
-    qk_products(kbuf(0), s_cur);
+    qk_products(slot_at(0), s_cur);
     __builtin_amdgcn_sched_barrier(0);
     wg_barrier();  // buffer 0 is refilled by block 0
 
     Cur cs{0, 0, 0, 0, nullptr};  // tile t (softmax, mask)
     seek(cs, 0);
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-    const int wrow0 = 32 * wave;      // this wave's first row, relative to the workgroup
-    const int myrow = wrow0 + l32;    // this lane's row, relative to the workgroup
+    const int wrow0 = 32 * wave;    // this wave's first row, relative to the workgroup
+    const int myrow = wrow0 + l32;  // this lane's row, relative to the workgroup
     for (int t = 0; t < n_tiles; ++t) {
       copy_slot(t + kBufs);
       __builtin_amdgcn_sched_barrier(0);
@@ -776,53 +528,12 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
       __builtin_amdgcn_sched_barrier(0);
       // interleaved: P.V of tile t-1, S of tile t+1, softmax of tile t
       const float mref = m2 == -INFINITY ? 0.f : m2;
-      pv_products(vbuf(t + 1), p_prev);
-      qk_products(kbuf(t + 1), s_nxt);
-      float rsq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int e = 2 * q;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][e & 15], c2s, -mref));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][(e & 15) + 1], c2s, -mref));
-        p_cur[q] = bf16x2{(__bf16)p0, (__bf16)p1};
-        rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p_cur[q], ones, rsq[q & 3], false);
-      }
-      float rs = (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
-#if RA_SP_SCHED == 2
-      __builtin_amdgcn_iglp_opt(2);
-#elif RA_SP_SCHED == 3
+      pv_products(slot_at(t + 1), p_prev);
+      qk_products(slot_at(t + 1), s_nxt);
+      float rs = softmax_exp(s_cur, c2s, mref, p_cur);
       __builtin_amdgcn_iglp_opt(3);
-#endif
       __builtin_amdgcn_sched_barrier(0);
-      // move the reference when the tile's sums overflow the bound, or the
-      // row has none yet (see softmax_step)
-      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) {
-        float mx = fmaxf(s_cur[0][0], s_cur[0][1]);
-#pragma unroll
-        for (int i = 2; i < 16; ++i) mx = fmaxf(mx, s_cur[0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s_cur[1][i]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m2, mx * c2s);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
-        m2 = m_new;
-        rsq[0] = rsq[1] = rsq[2] = rsq[3] = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int e = 2 * q;
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][e & 15], c2s, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[e >> 4][(e & 15) + 1], c2s, -m_use));
-          p_cur[q] = bf16x2{(__bf16)p0, (__bf16)p1};
-          rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p_cur[q], ones, rsq[q & 3], false);
-        }
-        rs = (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
-        lpart *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      }
+      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) rs = softmax_redo<C::DB>(s_cur, c2s, m2, lpart, acc, p_cur);
       lpart += rs;
       // slot t+2 (read by block t+1) has landed; kBufs-2 newer slots may fly
       wait_vm<(kBufs - 2) * 2 * DPW>();
@@ -834,12 +545,12 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
       step(cs, 0);
     }
     // P.V of the last tile (slot n+1 holds V_{n-1})
-    pv_products(vbuf(n_tiles + 1), p_prev);
+    pv_products(slot_at(n_tiles + 1), p_prev);
     __builtin_amdgcn_sched_barrier(0);
     wait_vm<0>();
   }
 
-  // ---- epilogue (as in the main kernel)
+  // ---- epilogue
   const float lsum = pair_sum(lpart);
   if (!row_ok) return;
   if (MODE == kInitStore || MODE == kLoadStore) {
@@ -878,27 +589,21 @@ __global__ __launch_bounds__(kSPThreads, 2) void attn_bf16_sp_kernel(AttnArgs a,
   }
 }
 
-#ifndef RA_KERNEL
-#define RA_KERNEL 1  // 0: one tile at a time, 4 waves; 1: software-pipelined, 8 waves
-#endif
-
 template <int D, typename OutT, int MODE>
 hipError_t launch_t(const AttnArgs& a, const BlockTable& t, hipStream_t s) {
-  const int bm = RA_KERNEL ? BMS : BM;
-  const int nthreads = RA_KERNEL ? kSPThreads : kThreads;
-  const int64_t n_qt = (a.q_len + bm - 1) / bm;
+  const int64_t n_qt = (a.q_len + BM - 1) / BM;
   const int64_t n_work = (int64_t)a.batch * a.heads * n_qt;
   if (n_work == 0) return hipSuccess;
   const int64_t per = (n_work + 7) / 8;
-  auto kern = RA_KERNEL ? attn_bf16_sp_kernel<D, OutT, MODE> : attn_bf16_kernel<D, OutT, MODE>;
-  const int lds_bytes = RA_KERNEL ? SpCfg<D>::LDS_BYTES : Cfg<D>::LDS_BYTES;
+  auto kern = attn_bf16_kernel<D, OutT, MODE>;
   static bool attr_done = false;  // set once per instantiation; the attribute is idempotent
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    hipError_t e =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<D>::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)(per * 8)), dim3(nthreads), lds_bytes, s, a, t);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per * 8)), dim3(kThreads), Cfg<D>::LDS_BYTES, s, a, t);
   return hipGetLastError();
 }
 

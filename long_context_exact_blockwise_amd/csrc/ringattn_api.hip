@@ -65,6 +65,9 @@ ra_status check_desc(const ra_desc* d) {
                     (long long)sts[t][i]);
     }
   }
+  // Key rows of a block may not overlap (the copies into LDS rely on it).
+  if (d->kv_len > 1 && d->kv_stride[1] < d->head_dim)
+    return fail(RA_E_SHAPE, "kv_stride[1] (%lld) must be >= head_dim", (long long)d->kv_stride[1]);
   // The kernels count keys of a block and tiles with 32-bit integers.
   if (d->kv_len >= ((int64_t)1 << 30))
     return fail(RA_E_UNSUPPORTED, "kv_len (%lld) must be below 2^30", (long long)d->kv_len);

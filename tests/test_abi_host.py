@@ -115,6 +115,7 @@ def _ring(d, q=FAKE, o=FAKE, lse=FAKE, kb=(FAKE,), vb=(FAKE,), pos=(0,), on_host
     (dict(kv_stride=(256 * 256, 0, 128)), ra.RA_E_SHAPE),    # zero stride along a dim of size > 1
     (dict(kv_stride=(256 * 256, 1 << 24, 128)), ra.RA_E_UNSUPPORTED),
     (dict(kv_len=1 << 30, kv_stride=(128, 128, 128)), ra.RA_E_UNSUPPORTED),  # keys per block must be < 2^30
+    (dict(kv_stride=(256 * 256, 64, 128)), ra.RA_E_SHAPE),   # key rows overlap (stride < head_dim)
     (dict(flags=4), ra.RA_E_UNSUPPORTED),
 ])
 def test_descriptor_rejected_before_enqueue(kw, status):
