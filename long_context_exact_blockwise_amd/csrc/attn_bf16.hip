@@ -81,6 +81,10 @@ struct Cfg {
     return (blk / DPW) * (2 * DPW * 1024) + (blk % DPW) * 1024 + (lin & 1023);
   }
   static __device__ __forceinline__ int v_at(int lin) { return k_at(lin) + DPW * 1024; }
+  // Slot offset of 8 key rows further down (the second half of a V^T
+  // fragment): doubled when 8 rows span a wave's DPW chunks, unchanged when
+  // they stay inside one wave's region.
+  static constexpr int HI8 = (8 * D * 2 / 1024 >= DPW) ? 2 * 8 * D * 2 : 8 * D * 2;
 };
 
 // Row-major placement of 16-byte chunk c of key row `key` in a tile.  K rows
@@ -193,8 +197,9 @@ __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint3
 // 1 KiB j) and the V base is passed 1 KiB DPW low.  Changing M0 while copies
 // are in flight stalls the wave, so it is set once per slot.
 template <int DPW>
-__device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbase_low, const uint32_t (&ko)[DPW],
+__device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbase, const uint32_t (&ko)[DPW],
                                              const uint32_t (&vo)[DPW], uint32_t m0) {
+  const char* vbase_low = vbase - DPW * 1024;  // V chunks use offsets 1 KiB (DPW + j)
   const uint64_t kb = (uint64_t)kbase, vb = (uint64_t)vbase_low;
   const uint32_t klo = __builtin_amdgcn_readfirstlane((uint32_t)kb);
   const uint32_t khi = __builtin_amdgcn_readfirstlane((uint32_t)(kb >> 32));
@@ -382,18 +387,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     // 64 lanes x 16 bytes: LDS chunk blk = wave*DPW + j of the row-major tile,
     // lane i fetching the global chunk that the swizzled layout puts at byte
     // 16 i of it.
-    uint32_t dk[DPW], dv[DPW], dkj[DPW], dvj[DPW];
+    // dkj / dvj: the offsets with the instruction offset 1 KiB j taken out
+    // (chunk j's key rows start at >= 1 KiB j of the source, a row being >=
+    // D*2 bytes, so they stay non-negative)
+    uint32_t dkj[DPW], dvj[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; ++j) {
       const int slot = (wave * DPW + j) * 64 + lane;
       const int key = slot / C::CH;
       const int cs = slot % C::CH;
-      dk[j] = (uint32_t)(key * a.kv_ss * 2 + (k_off<D>(key, cs) / 16 - key * C::CH) * 16);
-      dv[j] = (uint32_t)(key * a.kv_ss * 2 + (v_off<D>(key, cs) / 16 - key * C::CH) * 16);
-      // chunk j's key rows start at >= 1 KiB j of the source (a row is >= D*2
-      // bytes), so taking the instruction offset out stays non-negative
-      dkj[j] = dk[j] - 1024u * j;
-      dvj[j] = dv[j] - 1024u * j;
+      dkj[j] = (uint32_t)(key * a.kv_ss * 2 + (k_off<D>(key, cs) / 16 - key * C::CH) * 16) - 1024u * j;
+      dvj[j] = (uint32_t)(key * a.kv_ss * 2 + (v_off<D>(key, cs) / 16 - key * C::CH) * 16) - 1024u * j;
     }
     const uint32_t lds_base = lds_addr_of(lds);
     const uint32_t lds0 = lds_base + wave * (2 * DPW * 1024);  // this wave's region of a slot
@@ -404,7 +408,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
       for (int j = 0; j < DPW; ++j) {
         const int key = ((wave * DPW + j) * 64 + lane) / C::CH;
         const int last = kv_len - 1 - c.t * BN;
-        const uint32_t off = (is_v ? dv[j] : dk[j]) - (uint32_t)((key > last ? key - last : 0) * a.kv_ss * 2);
+        const uint32_t off =
+            (is_v ? dvj[j] : dkj[j]) + 1024u * j - (uint32_t)((key > last ? key - last : 0) * a.kv_ss * 2);
         lds_dma16(c.src, off, dst + (is_v ? DPW + j : j) * 1024);
       }
     };
@@ -417,7 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     auto copy_slot = [&](int s) {
       const uint32_t dst = lds0 + (uint32_t)((s % kBufs) * C::SLOT_BYTES);
       if (ck.t != ragged_t && cv.t != ragged_t) {
-        lds_dma_slot<DPW>(ck.src, cv.src - DPW * 1024, dkj, dvj, dst);
+        lds_dma_slot<DPW>(ck.src, cv.src, dkj, dvj, dst);
       } else {
         copy_ragged(ck, false, dst);
         copy_ragged(cv, true, dst);
@@ -439,8 +444,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     // columns 4s..4s+3 of a 16-column slice; it receives column (lane & 15)
     // of those 4 rows.  Rows 4*(g>>1) + t (+8 for the second load, +16 per
     // key step, +32 per key block), columns 32db + 16*(g&1) + 4s: vofs[db].
-    // Row offsets are multiples of 8 rows (of DPW KiB), which the slot layout
-    // doubles; they are instruction immediates.
+    // Row offsets of 16 and 32 rows are multiples of DPW KiB, which the slot
+    // layout doubles; 8 rows is C::HI8.  All are instruction immediates.
     int kofs[C::KS], vofs[C::DB];
     {
       const int kA = k_off<D>(l32, hf);
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
       // element by element from bit-cast 16-bit integers is miscompiled by
       // this toolchain, which drops half the elements.)
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)va);
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(va + 2 * 8 * ROWB));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(va + C::HI8));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
