@@ -9,8 +9,8 @@
  * next one is in flight ("Ring Attention with Blockwise Transformers for
  * Near-Infinite Context", Abstract), and the partial results are merged
  * through the state triple named in the "Gotchas and Failure Modes" section of
- * the tildalice page: running max m, running sum l and unnormalised output
- * acc.  After the last block the output is softmax(Q K^T * scale) V over every
+ * "Ring Attention: Train 1M Tokens on 8GB GPUs in 2026": running max m,
+ * running sum l and unnormalised output acc.  After the last block the output is softmax(Q K^T * scale) V over every
  * visible key (the attention equation of the section "Why Standard Attention
  * Explodes Past 100K Tokens", scale = 1/sqrt(d)) and LSE is its natural-log
  * log-sum-exp.  The merge is the exact online-softmax rule (Milakov and
@@ -21,11 +21,15 @@
  * Tensors and layout.
  *   Q, every K/V block and O are [B, S, H, D] with element strides
  *   (stride_b, stride_s, stride_h) and unit stride along D.  Query row r sits
- *   at global position q_pos0 + r; key j of a block at that block's
- *   kv_pos0 + j.  Causal masking: a key is visible iff its position <= the
- *   query's position (diagonal included).
+ *   at global position q_pos0 + r*s; key j of a block at that block's
+ *   kv_pos0 + j*s, where s = pos_stride (1 for contiguous chunks; P for the
+ *   striped order, in which device i of P holds tokens i, i+P, i+2P, ...).
+ *   Causal masking: a key is visible iff its position <= the query's
+ *   position (diagonal included).
  *   State: m, l  [B, H, Sq] fp32 contiguous; acc [B, H, Sq, D] fp32
- *   contiguous; m is in natural-log score units (max of scale * q.k).
+ *   contiguous; m is in natural-log score units, a reference point at or
+ *   below the running max of scale * q.k (the kernels move it only when the
+ *   sums would grow too large).
  *   LSE [B, H, Sq] fp32 contiguous.  A row that has seen no visible key has
  *   m = -inf, l = 0, acc = 0, and is finalized to O = 0, LSE = -inf.
  *   The state triple is defined up to the choice of m: any (m, l, acc) with
@@ -62,7 +66,7 @@
 extern "C" {
 #endif
 
-#define RINGATTN_ABI_VERSION 1
+#define RINGATTN_ABI_VERSION 2
 
 typedef enum ra_status {
   RA_OK = 0,
@@ -86,7 +90,7 @@ typedef struct ra_desc {
   int32_t head_dim;    /* D: 64 or 128                                        */
   int32_t causal;      /* 1: key visible iff kv_pos <= q_pos; 0: all visible   */
   int64_t q_len;       /* Sq >= 0: rows of the local query chunk              */
-  int64_t kv_len;      /* Ck >= 0: keys per KV block (all blocks equal), < 2^30 */
+  int64_t kv_len;      /* Ck >= 0: key capacity of a KV block, < 2^30         */
   int64_t q_pos0;      /* global position of query row 0 (q_idx * Sq)         */
   float scale;         /* softmax temperature; <= 0 selects 1/sqrt(D)         */
   int32_t in_dtype;    /* ra_dtype of Q, K, V                                 */
@@ -95,6 +99,8 @@ typedef struct ra_desc {
   int64_t q_stride[3]; /* element strides of Q along (b, s, h)                */
   int64_t kv_stride[3];/* element strides of every K and V block; (s) >= D   */
   int64_t o_stride[3]; /* element strides of O                                */
+  int64_t pos_stride;  /* position step between rows and between keys; 0 or 1:
+                          contiguous, P: striped order over P devices          */
 } ra_desc;
 
 /* Block classes returned by ringattn_block_class. */
@@ -112,24 +118,27 @@ const char* ringattn_status_str(int status);
 /* Detail of the last failing call on this thread ("" if none). */
 const char* ringattn_last_error(void);
 
-/* Ring schedule of the tildalice page, section "Ring Attention: Partition
+/* Ring schedule of "Ring Attention: Train 1M Tokens on 8GB GPUs in 2026",
+ * section "Ring Attention: Partition
  * Sequence Length, Not Batch": at step s the device at ring index q_idx holds
  * the block that started on device (q_idx - s) mod P.  Writes that block index
  * for s = 0..P-1 into order[P] (host memory).  Host only. */
 ra_status ringattn_ring_order(int32_t q_idx, int32_t num_devices, int32_t* order);
 
-/* Causal class of the block starting at kv_pos0 with respect to the query
- * chunk of desc (RA_BLOCK_*); non-causal descriptors give RA_BLOCK_FULL for a
- * non-empty block.  Empty chunks or blocks give RA_BLOCK_SKIP.  Host only;
- * returns -1 for a NULL desc. */
+/* Causal class of the block of kv_len keys starting at kv_pos0 with respect to
+ * the query chunk of desc (RA_BLOCK_*), positions stepping by pos_stride;
+ * non-causal descriptors give RA_BLOCK_FULL for a non-empty block.  Empty
+ * chunks or blocks give RA_BLOCK_SKIP.  Host only; returns -1 for a NULL desc
+ * or a negative pos_stride. */
 int32_t ringattn_block_class(const ra_desc* desc, int64_t kv_pos0);
 
 /* Start a ring pass: m = -inf, l = 0, acc = 0 (device pointers, layouts above). */
 ra_status ringattn_init_state(const ra_desc* desc, float* m, float* l, float* acc, hipStream_t stream);
 
-/* Attend the query chunk q to one KV block (device pointers k, v whose keys
- * sit at kv_pos0 + 0..kv_len-1) and fold the result into (m, l, acc) by the
- * online-softmax rule.  A block with no key visible to any row enqueues
+/* Attend the query chunk q to one KV block (device pointers k, v whose kv_len
+ * keys sit at kv_pos0 + j*pos_stride) and fold the result into (m, l, acc) by
+ * the online-softmax rule.  A block with fewer valid keys is passed with
+ * kv_len set to that count.  A block with no key visible to any row enqueues
  * nothing and returns RA_OK. */
 ra_status ringattn_block_fwd(const ra_desc* desc, const void* q, const void* k, const void* v, int64_t kv_pos0,
                              float* m, float* l, float* acc, hipStream_t stream);
@@ -140,11 +149,16 @@ ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l,
                             float* lse, hipStream_t stream);
 
 /* Whole ring pass over num_blocks >= 0 blocks given in processing (ring) order:
- * k_blocks[i], v_blocks[i] hold the keys at kv_pos0[i] + 0..kv_len-1.  The
- * arrays k_blocks, v_blocks, kv_pos0 are host memory.  Equivalent to
- * init_state, block_fwd for each block in array order, finalize; the fused
- * path keeps the state on chip and may differ from the per-block path only by
- * rounding.
+ * k_blocks[i], v_blocks[i] hold the keys at kv_pos0[i] + j*pos_stride.
+ * kv_valid: NULL when every block holds kv_len keys; otherwise block i holds
+ * kv_valid[i] valid keys (0 <= kv_valid[i] <= kv_len) at its start and the
+ * rest of its kv_len rows is padding, never attended (per-block valid
+ * lengths: chunks of unequal length, as the FAQ of "Ring Attention: Train 1M
+ * Tokens on 8GB GPUs in 2026" describes, without padded work).  The arrays
+ * k_blocks, v_blocks, kv_pos0, kv_valid are host memory.  Equivalent to
+ * init_state, block_fwd for each block in array order (with kv_len =
+ * kv_valid[i]), finalize; the fused path keeps the state on chip and may
+ * differ from the per-block path only by rounding.
  *
  * kv_on_host = 0: blocks are device memory.  Unless flags has
  *   RA_FLAG_PERBLOCK, a fused kernel runs (m, l, acc may be NULL when
@@ -159,7 +173,8 @@ ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l,
  *   alive and unchanged until the compute stream has finished.
  * O and LSE are written on `compute`. */
 ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* const* k_blocks,
-                            const void* const* v_blocks, const int64_t* kv_pos0, int32_t num_blocks,
+                            const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
+                            int32_t num_blocks,
                             int32_t kv_on_host, void* const* stage_k, void* const* stage_v, float* m, float* l,
                             float* acc, void* o, float* lse, hipStream_t compute, hipStream_t copy);
 

@@ -12,7 +12,7 @@
 //   S^T[64 keys x 32 rows] = K . Q^T      v_mfma_f32_32x32x16_bf16, K from LDS,
 //                                         Q fragments held in registers
 //   causal / ragged mask (diagonal and tail tiles only)
-//   p = exp2(S*c - m); l += sum p         c = scale*log2(e), m a reference
+//   p = exp2(S*c - m); l += sum p (fp32)  c = scale*log2(e), m a reference
 //                                         point (see softmax_redo)
 //   O^T[D x 32 rows] += V^T . P^T         v_mfma_f32_32x32x16_bf16, V^T gathered
 //                                         from LDS with ds_read_b64_tr_b16
@@ -119,10 +119,11 @@ constexpr float kPLim = 4096.0f;
 
 // Exponentiate the 32 raw scores q.k (two f32x16 fragments of S^T) this lane
 // holds for its query row against reference mref (log2 units): bf16 pairs
-// p[q] = (p_{2q}, p_{2q+1}) for the P.V product; returns their sum (of the
-// same bf16 values).  The other 32 keys of the tile sit in the lane 32 away.
+// p[q] = (p_{2q}, p_{2q+1}) for the P.V product; returns the fp32 sum of the
+// unrounded values (the row sum, hence LSE, keeps fp32 accuracy; O then
+// differs from an exactly normalised bf16-P average by at most the bf16
+// rounding of P).  The other 32 keys of the tile sit in the lane 32 away.
 __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c2, float mref, bf16x2 (&p)[16]) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   float rsq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -130,7 +131,7 @@ __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c2, flo
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c2, -mref));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][(e & 15) + 1], c2, -mref));
     p[q] = bf16x2{(__bf16)p0, (__bf16)p1};
-    rsq[q & 3] = __builtin_amdgcn_fdot2_f32_bf16(p[q], ones, rsq[q & 3], false);
+    rsq[q & 3] += p0 + p1;
   }
   return (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
 }
@@ -261,9 +262,10 @@ struct RowRange {
   int64_t first_pos, last_pos;  // global positions of the workgroup's first / last valid row
 };
 
-// Number of BN-key tiles of a block that some row of the workgroup can see.
-__device__ __forceinline__ int block_tiles(const AttnArgs& a, int64_t pos0, const RowRange& rr) {
-  int64_t nk = a.kv_len;
+// Number of BN-key tiles of a block (len valid keys from pos0) that some row of
+// the workgroup can see.
+__device__ __forceinline__ int block_tiles(const AttnArgs& a, int64_t pos0, int len, const RowRange& rr) {
+  int64_t nk = len;
   if (a.causal) {
     int64_t lim = rr.last_pos - pos0 + 1;
     nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
@@ -304,10 +306,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
   rr.first_pos = a.q_pos0 + row0;
   rr.last_pos = a.q_pos0 + ((row0 + BM < a.q_len) ? row0 + BM : a.q_len) - 1;
   const float c2s = a.scale * kLog2e;
-  const int kv_len = (int)a.kv_len;  // < 2^30 (checked on the host)
 
   int n_tiles = 0;
-  for (int bi = 0; bi < a.nblocks; ++bi) n_tiles += block_tiles(a, tbl.pos0[bi], rr);
+  for (int bi = 0; bi < a.nblocks; ++bi) n_tiles += block_tiles(a, tbl.pos0[bi], tbl.len[bi], rr);
   // A per-block launch (state in HBM) whose rows see no key of the block
   // leaves the state untouched.
   if (MODE == kLoadStore && n_tiles == 0) return;
@@ -351,19 +352,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
 
   if (n_tiles > 0) {
     // ---- tile cursors (all wave-uniform, scalar): block, tile, visible tile
-    // count, position of the tile's key 0 relative to the workgroup's first
-    // row (clamped below: far-away tiles are fully visible) and, for the copy
-    // cursors, the global address of the tile for this (b, h).
+    // count, the block's valid keys (< 2^30, checked on the host) and its
+    // ragged last tile (-1: none), position of the tile's key 0 relative to
+    // the workgroup's first row (clamped below: far-away tiles are fully
+    // visible) and, for the copy cursors, the global address of the tile for
+    // this (b, h).
     struct Cur {
-      int b, t, n, rel;
+      int b, t, n, len, ragged, rel;
       const char* src;
     };
     const int64_t kv_head_off = ((int64_t)b * a.kv_sb + (int64_t)h * a.kv_sh) * 2;
     const int64_t tile_bytes_g = (int64_t)BN * a.kv_ss * 2;
     auto seek = [&](Cur& c, int which) {  // which: 0 none, 1 K, 2 V
-      while (c.b < a.nblocks && (c.n = block_tiles(a, tbl.pos0[c.b], rr)) == 0) ++c.b;
+      while (c.b < a.nblocks && (c.n = block_tiles(a, tbl.pos0[c.b], tbl.len[c.b], rr)) == 0) ++c.b;
       c.t = 0;
       if (c.b < a.nblocks) {
+        c.len = tbl.len[c.b];
+        c.ragged = (c.len & (BN - 1)) ? (c.len >> 6) : -1;  // the ragged tile of a block is its last one
         // visible tiles start at or before the last row; far below, clamp so
         // that rel + 64 t stays far below for every tile of the block
         const int64_t rel = tbl.pos0[c.b] - rr.first_pos;
@@ -380,8 +385,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
         seek(c, which);
       }
     };
-    // The ragged tile of a block (keys past kv_len) is its last one.
-    const int ragged_t = (kv_len & (BN - 1)) ? (kv_len >> 6) : -1;
 
     // ---- copies into LDS.  Copy j of a wave's K (or V) share moves 1 KiB =
     // 64 lanes x 16 bytes: LDS chunk blk = wave*DPW + j of the row-major tile,
@@ -407,7 +410,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
 #pragma unroll
       for (int j = 0; j < DPW; ++j) {
         const int key = ((wave * DPW + j) * 64 + lane) / C::CH;
-        const int last = kv_len - 1 - c.t * BN;
+        const int last = c.len - 1 - c.t * BN;
         const uint32_t off =
             (is_v ? dvj[j] : dkj[j]) + 1024u * j - (uint32_t)((key > last ? key - last : 0) * a.kv_ss * 2);
         lds_dma16(c.src, off, dst + (is_v ? DPW + j : j) * 1024);
@@ -415,13 +418,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     };
     // copy cursors: K of slot s is tile min(s, n-1); V of slot s is tile
     // clamp(s-2, 0, n-1)
-    Cur ck{0, 0, 0, 0, nullptr}, cv{0, 0, 0, 0, nullptr};
+    Cur ck{0, 0, 0, 0, 0, 0, nullptr}, cv{0, 0, 0, 0, 0, 0, nullptr};
     seek(ck, 1);
     seek(cv, 2);
     int kidx = 0, vidx = 0;
     auto copy_slot = [&](int s) {
       const uint32_t dst = lds0 + (uint32_t)((s % kBufs) * C::SLOT_BYTES);
-      if (ck.t != ragged_t && cv.t != ragged_t) {
+      if (ck.t != ck.ragged && cv.t != cv.ragged) {
         lds_dma_slot<DPW>(ck.src, cv.src, dkj, dvj, dst);
       } else {
         copy_ragged(ck, false, dst);
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     __builtin_amdgcn_sched_barrier(0);
     wg_barrier();  // buffer 0 is refilled by block 0
 
-    Cur cs{0, 0, 0, 0, nullptr};  // tile t (softmax, mask)
+    Cur cs{0, 0, 0, 0, 0, 0, nullptr};  // tile t (softmax, mask)
     seek(cs, 0);
     const int wrow0 = 32 * wave;    // this wave's first row, relative to the workgroup
     const int myrow = wrow0 + l32;  // this lane's row, relative to the workgroup
@@ -517,8 +520,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
       __builtin_amdgcn_sched_barrier(0);
       // mask keys past the block end and (causal) keys after this lane's row:
       // key k of the tile is live iff k < thr
-      if (cs.t == ragged_t || (a.causal && cs.rel + (BN - 1) > wrow0)) {
-        int lim = cs.t == ragged_t ? kv_len - cs.t * BN : BN;
+      if (cs.t == cs.ragged || (a.causal && cs.rel + (BN - 1) > wrow0)) {
+        int lim = cs.t == cs.ragged ? cs.len - cs.t * BN : BN;
         if (a.causal) {
           const int lc = myrow - cs.rel + 1;
           lim = lc < lim ? lc : lim;

@@ -17,8 +17,8 @@ namespace {
 constexpr int kRows = 64;  // rows (threads) per workgroup
 constexpr int BN = 16;     // keys per tile
 
-__device__ __forceinline__ int tiles_for(const AttnArgs& a, int64_t pos0, int64_t last_pos) {
-  int64_t nk = a.kv_len;
+__device__ __forceinline__ int tiles_for(const AttnArgs& a, int64_t pos0, int len, int64_t last_pos) {
+  int64_t nk = len;
   if (a.causal) {
     const int64_t lim = last_pos - pos0 + 1;
     nk = lim < 0 ? 0 : (lim < nk ? lim : nk);
@@ -70,7 +70,8 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a, BlockTable 
 
   for (int bi = 0; bi < a.nblocks; ++bi) {
     const int64_t pos0 = tbl.pos0[bi];
-    const int nt = tiles_for(a, pos0, last_pos);
+    const int64_t len = tbl.len[bi];  // valid keys of the block
+    const int nt = tiles_for(a, pos0, (int)len, last_pos);
     const float* kb = (const float*)tbl.k[bi] + b * a.kv_sb + h * a.kv_sh;
     const float* vb = (const float*)tbl.v[bi] + b * a.kv_sb + h * a.kv_sh;
     for (int t = 0; t < nt; ++t) {
@@ -78,8 +79,8 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a, BlockTable 
       for (int e = tid; e < BN * D; e += kRows) {
         const int j = e / D, d = e % D;
         const int64_t kk = (int64_t)t * BN + j;
-        ks[j][d] = kk < a.kv_len ? kb[kk * a.kv_ss + d] : 0.f;
-        vs[j][d] = kk < a.kv_len ? vb[kk * a.kv_ss + d] : 0.f;
+        ks[j][d] = kk < len ? kb[kk * a.kv_ss + d] : 0.f;
+        vs[j][d] = kk < len ? vb[kk * a.kv_ss + d] : 0.f;
       }
       __syncthreads();
       // pass 1: the tile's largest visible score
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a, BlockTable 
 #pragma unroll 1
       for (int j = 0; j < BN; ++j) {
         const int64_t kk = (int64_t)t * BN + j;
-        if (kk < a.kv_len && (!a.causal || pos0 + kk <= my_pos)) {
+        if (kk < len && (!a.causal || pos0 + kk <= my_pos)) {
           mt = fmaxf(mt, score(j));
           ++nlive;
         }
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kRows) void attn_f32_kernel(AttnArgs a, BlockTable 
 #pragma unroll 1
       for (int j = 0; j < BN; ++j) {
         const int64_t kk = (int64_t)t * BN + j;
-        if (kk < a.kv_len && (!a.causal || pos0 + kk <= my_pos)) {
+        if (kk < len && (!a.causal || pos0 + kk <= my_pos)) {
           const float p = expf(score(j) - m_new);
           l += p;
 #pragma unroll

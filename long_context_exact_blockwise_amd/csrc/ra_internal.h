@@ -14,7 +14,8 @@ namespace ra {
 struct BlockTable {
   const void* k[RA_FUSED_MAX_BLOCKS];
   const void* v[RA_FUSED_MAX_BLOCKS];
-  int64_t pos0[RA_FUSED_MAX_BLOCKS];
+  int64_t pos0[RA_FUSED_MAX_BLOCKS];  // position of key 0 in row units (contiguous-equivalent, see the API layer)
+  int32_t len[RA_FUSED_MAX_BLOCKS];   // valid keys of the block (<= kv_len)
 };
 
 // How a launch starts and ends its rows' state.

@@ -45,6 +45,7 @@ ra_status check_desc(const ra_desc* d) {
   if (d->q_len < 0 || d->kv_len < 0)
     return fail(RA_E_SHAPE, "q_len (%lld) and kv_len (%lld) must be >= 0", (long long)d->q_len, (long long)d->kv_len);
   if (d->causal != 0 && d->causal != 1) return fail(RA_E_SHAPE, "causal must be 0 or 1 (got %d)", d->causal);
+  if (d->pos_stride < 0) return fail(RA_E_SHAPE, "pos_stride must be >= 0 (got %lld)", (long long)d->pos_stride);
   if (std::isnan(d->scale) || std::isinf(d->scale)) return fail(RA_E_SHAPE, "scale must be finite");
   if ((d->flags & ~RA_FLAG_PERBLOCK) != 0) return fail(RA_E_UNSUPPORTED, "unknown flags 0x%x", d->flags);
   const bool ok_dt = (d->in_dtype == RA_F32 && d->out_dtype == RA_F32) ||
@@ -104,11 +105,22 @@ ra_status check_mem(const void* p, bool want_host, const char* name) {
   return RA_OK;
 }
 
-int32_t classify(const ra_desc* d, int64_t kv_pos0) {
-  if (d->q_len == 0 || d->kv_len == 0) return RA_BLOCK_SKIP;
+// Positions in row units.  With pos_stride s > 1, row r sits at q_pos0 + r s
+// and key j at kv_pos0 + j s; key j is visible to row r iff
+// j - r <= floor((q_pos0 - kv_pos0) / s), which is the contiguous rule for a
+// query chunk at 0 and a block at -floor((q_pos0 - kv_pos0) / s).  The kernels
+// only ever see these contiguous-equivalent positions.
+int64_t floor_div(int64_t a, int64_t b) { return a / b - ((a % b != 0) && ((a < 0) != (b < 0))); }
+int64_t q_pos_eff(const ra_desc* d) { return d->pos_stride > 1 ? 0 : d->q_pos0; }
+int64_t kv_pos_eff(const ra_desc* d, int64_t kv_pos0) {
+  return d->pos_stride > 1 ? -floor_div(d->q_pos0 - kv_pos0, d->pos_stride) : kv_pos0;
+}
+
+int32_t classify(const ra_desc* d, int64_t kv_pos0, int64_t len) {
+  if (d->q_len == 0 || len == 0) return RA_BLOCK_SKIP;
   if (!d->causal) return RA_BLOCK_FULL;
-  const int64_t q_first = d->q_pos0, q_last = d->q_pos0 + d->q_len - 1;
-  const int64_t k_first = kv_pos0, k_last = kv_pos0 + d->kv_len - 1;
+  const int64_t q_first = q_pos_eff(d), q_last = q_first + d->q_len - 1;
+  const int64_t k_first = kv_pos_eff(d, kv_pos0), k_last = k_first + len - 1;
   if (k_first > q_last) return RA_BLOCK_SKIP;
   if (k_last <= q_first) return RA_BLOCK_FULL;
   return RA_BLOCK_DIAG;
@@ -134,7 +146,7 @@ AttnArgs make_args(const ra_desc* d, const void* q, void* o, float* lse, float* 
   a.o_sh = d->o_stride[2];
   a.q_len = d->q_len;
   a.kv_len = d->kv_len;
-  a.q_pos0 = d->q_pos0;
+  a.q_pos0 = q_pos_eff(d);
   a.batch = d->batch;
   a.heads = d->heads;
   a.head_dim = d->head_dim;
@@ -220,8 +232,8 @@ ra_status ringattn_ring_order(int32_t q_idx, int32_t num_devices, int32_t* order
 }
 
 int32_t ringattn_block_class(const ra_desc* desc, int64_t kv_pos0) {
-  if (!desc) return -1;
-  return classify(desc, kv_pos0);
+  if (!desc || desc->pos_stride < 0) return -1;
+  return classify(desc, kv_pos0, desc->kv_len);
 }
 
 ra_status ringattn_init_state(const ra_desc* desc, float* m, float* l, float* acc, hipStream_t stream) {
@@ -250,12 +262,13 @@ ra_status ringattn_block_fwd(const ra_desc* desc, const void* q, const void* k, 
   if ((st = check_mem(k, false, "k")) != RA_OK) return st;
   if ((st = check_mem(v, false, "v")) != RA_OK) return st;
   if ((st = check_state_mem(m, l, acc)) != RA_OK) return st;
-  if (classify(desc, kv_pos0) == RA_BLOCK_SKIP) return RA_OK;
+  if (classify(desc, kv_pos0, desc->kv_len) == RA_BLOCK_SKIP) return RA_OK;
   BlockTable t;
   std::memset(&t, 0, sizeof t);
   t.k[0] = k;
   t.v[0] = v;
-  t.pos0[0] = kv_pos0;
+  t.pos0[0] = kv_pos_eff(desc, kv_pos0);
+  t.len[0] = (int32_t)desc->kv_len;
   AttnArgs a = make_args(desc, q, nullptr, nullptr, m, l, acc);
   hipError_t e = launch_attn(desc, a, t, 1, ra::kLoadStore, stream);
   return e == hipSuccess ? RA_OK : hip_fail(e, "block kernel launch");
@@ -279,7 +292,8 @@ ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l,
 }
 
 ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* const* k_blocks,
-                            const void* const* v_blocks, const int64_t* kv_pos0, int32_t num_blocks,
+                            const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
+                            int32_t num_blocks,
                             int32_t kv_on_host, void* const* stage_k, void* const* stage_v, float* m, float* l,
                             float* acc, void* o, float* lse, hipStream_t compute, hipStream_t copy) {
   g_err.clear();
@@ -295,12 +309,16 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
     return fail(RA_E_NULL, "k_blocks, v_blocks and kv_pos0 are required when num_blocks > 0");
 
   // Blocks that some row can see, in the given order.
+  auto valid = [&](int i) -> int64_t { return kv_valid ? kv_valid[i] : desc->kv_len; };
   std::vector<int> live;
   live.reserve(num_blocks);
   for (int i = 0; i < num_blocks; ++i) {
     if ((st = need_ptr(k_blocks[i], "k_blocks[i]")) != RA_OK) return st;
     if ((st = need_ptr(v_blocks[i], "v_blocks[i]")) != RA_OK) return st;
-    if (classify(desc, kv_pos0[i]) != RA_BLOCK_SKIP) live.push_back(i);
+    if (valid(i) < 0 || valid(i) > desc->kv_len)
+      return fail(RA_E_SHAPE, "kv_valid[%d] = %lld must be in [0, kv_len = %lld]", i, (long long)valid(i),
+                  (long long)desc->kv_len);
+    if (classify(desc, kv_pos0[i], valid(i)) != RA_BLOCK_SKIP) live.push_back(i);
   }
   const bool perblock = kv_on_host || (desc->flags & RA_FLAG_PERBLOCK);
   const bool needs_ws = perblock || (int)live.size() > RA_FUSED_MAX_BLOCKS;
@@ -349,7 +367,8 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
       for (int j = 0; j < nlive; ++j) {
         t.k[j] = k_blocks[live[j]];
         t.v[j] = v_blocks[live[j]];
-        t.pos0[j] = kv_pos0[live[j]];
+        t.pos0[j] = kv_pos_eff(desc, kv_pos0[live[j]]);
+        t.len[j] = (int32_t)valid(live[j]);
       }
       e = launch_attn(desc, a, t, nlive, ra::kInitFinalize, compute);
       return e == hipSuccess ? RA_OK : hip_fail(e, "fused kernel launch");
@@ -359,7 +378,8 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
       for (int j = 0; j < n; ++j) {
         t.k[j] = k_blocks[live[s0 + j]];
         t.v[j] = v_blocks[live[s0 + j]];
-        t.pos0[j] = kv_pos0[live[s0 + j]];
+        t.pos0[j] = kv_pos_eff(desc, kv_pos0[live[s0 + j]]);
+        t.len[j] = (int32_t)valid(live[s0 + j]);
       }
       const bool first = s0 == 0, last = s0 + n >= nlive;
       const int mode = first ? ra::kInitStore : (last ? ra::kLoadFinalize : ra::kLoadStore);
@@ -376,7 +396,8 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
     for (int i : live) {
       t.k[0] = k_blocks[i];
       t.v[0] = v_blocks[i];
-      t.pos0[0] = kv_pos0[i];
+      t.pos0[0] = kv_pos_eff(desc, kv_pos0[i]);
+      t.len[0] = (int32_t)valid(i);
       e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
       if (e != hipSuccess) return hip_fail(e, "block kernel launch");
     }
@@ -401,7 +422,8 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
         return hip_fail(e, "hipStreamWaitEvent");
       t.k[0] = stage_k[slot];
       t.v[0] = stage_v[slot];
-      t.pos0[0] = kv_pos0[i];
+      t.pos0[0] = kv_pos_eff(desc, kv_pos0[i]);
+      t.len[0] = (int32_t)valid(i);
       e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
       if (e != hipSuccess) return hip_fail(e, "block kernel launch");
       if ((e = hipEventRecord(g_ev.free_[slot], compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");

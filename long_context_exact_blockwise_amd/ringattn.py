@@ -24,6 +24,7 @@ RA_F32, RA_BF16 = 0, 1
 RA_FLAG_PERBLOCK = 1
 RA_BLOCK_SKIP, RA_BLOCK_FULL, RA_BLOCK_DIAG = 0, 1, 2
 RA_FUSED_MAX_BLOCKS = 64
+ABI_VERSION = 2
 
 SYMBOLS = (
     "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
@@ -45,6 +46,7 @@ class RaDesc(ctypes.Structure):
         ("q_pos0", ctypes.c_int64), ("scale", ctypes.c_float), ("in_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("pos_stride", ctypes.c_int64),
     ]
 
 
@@ -78,11 +80,11 @@ def lib():
     L.ringattn_finalize.argtypes = [D, P, P, P, P, P, P]
     L.ringattn_ring_fwd.restype = ctypes.c_int
     L.ringattn_ring_fwd.argtypes = [D, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(ctypes.c_int64),
-                                    ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(P), ctypes.POINTER(P),
-                                    P, P, P, P, P, P, P]
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.POINTER(P), ctypes.POINTER(P), P, P, P, P, P, P, P]
     L.ringattn_probe_copy.restype = ctypes.c_int
     L.ringattn_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
-    if L.ringattn_abi_version() != 1:
+    if L.ringattn_abi_version() != ABI_VERSION:
         raise RuntimeError("libringattn.so ABI version mismatch")
     _lib = L
     return L
@@ -114,9 +116,11 @@ def _stream(s) -> ctypes.c_void_p:
 
 
 def make_desc(q: torch.Tensor, kv_block: torch.Tensor, o: Optional[torch.Tensor] = None, *, q_pos0: int = 0,
-              causal: bool = False, scale: float = 0.0, flags: int = 0, out_dtype=None) -> RaDesc:
+              causal: bool = False, scale: float = 0.0, flags: int = 0, out_dtype=None,
+              pos_stride: int = 1) -> RaDesc:
     """Descriptor from tensors in [B, S, H, D] layout (strides taken as given;
-    the D stride must be 1).  kv_block is any one KV block (all share strides)."""
+    the D stride must be 1).  kv_block is any one KV block (all share strides
+    and the key capacity kv_len)."""
     b, sq, h, d = q.shape
     kb, ck, kh, kd = kv_block.shape
     if (kb, kh, kd) != (b, h, d):
@@ -133,6 +137,7 @@ def make_desc(q: torch.Tensor, kv_block: torch.Tensor, o: Optional[torch.Tensor]
         out_dtype = o.dtype if o is not None else q.dtype
     desc.out_dtype = _dt(out_dtype)
     desc.flags = flags
+    desc.pos_stride = pos_stride
     for i in range(3):
         desc.q_stride[i] = q.stride(i)
         desc.kv_stride[i] = kv_block.stride(i)
@@ -165,20 +170,21 @@ def ringattn_finalize(desc: RaDesc, m, l, acc, o, lse, stream=None):
 
 
 def ringattn_ring_fwd(desc: RaDesc, q, k_blocks: Sequence, v_blocks: Sequence, kv_pos0: Sequence[int], o, lse,
-                      m=None, l=None, acc=None, *, kv_on_host: bool = False, stage_k: Sequence = None,
-                      stage_v: Sequence = None, stream=None, copy_stream=None):
+                      m=None, l=None, acc=None, *, kv_valid: Optional[Sequence[int]] = None, kv_on_host: bool = False,
+                      stage_k: Sequence = None, stage_v: Sequence = None, stream=None, copy_stream=None):
     n = len(k_blocks)
     P = ctypes.c_void_p
     kp = (P * max(n, 1))(*[t.data_ptr() for t in k_blocks])
     vp = (P * max(n, 1))(*[t.data_ptr() for t in v_blocks])
     pp = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_pos0])
+    nv = None if kv_valid is None else (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_valid])
     sk = sv = None
     if stage_k is not None:
         sk = (P * 2)(*[t.data_ptr() for t in stage_k])
         sv = (P * 2)(*[t.data_ptr() for t in stage_v])
     cs = _stream(copy_stream) if copy_stream is not None else None
-    _check(lib().ringattn_ring_fwd(ctypes.byref(desc), _ptr(q), kp, vp, pp, n, 1 if kv_on_host else 0, sk, sv,
-                                   _ptr(m), _ptr(l), _ptr(acc), _ptr(o), _ptr(lse), _stream(stream), cs))
+    _check(lib().ringattn_ring_fwd(ctypes.byref(desc), _ptr(q), kp, vp, pp, nv, n, 1 if kv_on_host else 0, sk,
+                                   sv, _ptr(m), _ptr(l), _ptr(acc), _ptr(o), _ptr(lse), _stream(stream), cs))
 
 
 def ringattn_probe_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
@@ -197,9 +203,11 @@ def state_buffers(desc: RaDesc, device):
 
 def ring_forward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: Sequence[torch.Tensor],
                  kv_pos0: Sequence[int], *, q_pos0: int = 0, causal: bool = False, scale: float = 0.0,
-                 perblock: bool = False, out_dtype=None, o=None, lse=None, workspace=None):
-    """Attention of q over the blocks (device tensors) in the given order.
-    Returns (O [B, Sq, H, D], LSE [B, H, Sq] fp32)."""
+                 perblock: bool = False, out_dtype=None, o=None, lse=None, workspace=None,
+                 kv_valid: Optional[Sequence[int]] = None, pos_stride: int = 1):
+    """Attention of q over the blocks (device tensors) in the given order;
+    block i contributes its first kv_valid[i] keys (all when kv_valid is
+    None).  Returns (O [B, Sq, H, D], LSE [B, H, Sq] fp32)."""
     out_dtype = out_dtype or q.dtype
     b, sq, h, d = q.shape
     if o is None:
@@ -207,14 +215,14 @@ def ring_forward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: Se
     if lse is None:
         lse = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
     desc = make_desc(q, k_blocks[0] if len(k_blocks) else q, o, q_pos0=q_pos0, causal=causal, scale=scale,
-                     flags=RA_FLAG_PERBLOCK if perblock else 0)
+                     flags=RA_FLAG_PERBLOCK if perblock else 0, pos_stride=pos_stride)
     if len(k_blocks) == 0:
         desc.kv_len = 0
     need_ws = perblock or len(k_blocks) > RA_FUSED_MAX_BLOCKS
     m = l = acc = None
     if need_ws:
         m, l, acc = workspace if workspace is not None else state_buffers(desc, q.device)
-    ringattn_ring_fwd(desc, q, k_blocks, v_blocks, kv_pos0, o, lse, m, l, acc)
+    ringattn_ring_fwd(desc, q, k_blocks, v_blocks, kv_pos0, o, lse, m, l, acc, kv_valid=kv_valid)
     return o, lse
 
 

@@ -19,7 +19,8 @@ What it computes, and from which passage:
   approximation).  Causal masking and the log-sum-exp are not defined on the
   pages; their readings are stated on each function.
 * ``partial_state``: the (running max, running sum, unnormalised output)
-  triple the "Gotchas and Failure Modes" section of the tildalice page names as
+  triple the "Gotchas and Failure Modes" section of "Ring Attention: Train 1M
+  Tokens on 8GB GPUs in 2026" names as
   the state carried across chunks, written as its closed form over the blocks
   processed so far (not as an iteration), following the online-normaliser idea
   of Milakov & Gimelshein cited in the arXiv record's reference list.

@@ -82,8 +82,9 @@ def attention_rows(q, k, v, q_pos, kv_pos, causal: bool, scale: float):
     return out, lse
 
 
-def _gather_blocks(k_blocks, v_blocks, kv_pos0s):
-    """Concatenate KV blocks in global-position order with their positions."""
+def _gather_blocks(k_blocks, v_blocks, kv_pos0s, pos_stride=1):
+    """Concatenate KV blocks with their global key positions (block j's key i
+    sits at kv_pos0s[j] + i * pos_stride)."""
     order = sorted(range(len(k_blocks)), key=lambda j: int(kv_pos0s[j]))
     ks, vs, ps = [], [], []
     for j in order:
@@ -91,20 +92,27 @@ def _gather_blocks(k_blocks, v_blocks, kv_pos0s):
         vb = np.asarray(v_blocks[j], dtype=np.float64)
         ks.append(kb)
         vs.append(vb)
-        ps.append(int(kv_pos0s[j]) + np.arange(kb.shape[1], dtype=np.int64))
+        ps.append(int(kv_pos0s[j]) + int(pos_stride) * np.arange(kb.shape[1], dtype=np.int64))
     return ks, vs, ps
 
 
 def ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int,
                    kv_pos0s: Sequence[int], causal: bool, scale: float | None = None,
-                   rows: Sequence[int] | None = None, heads: Sequence[int] | None = None):
+                   rows: Sequence[int] | None = None, heads: Sequence[int] | None = None,
+                   pos_stride: int = 1):
     """Exact attention of one device's query chunk over all KV blocks it receives.
 
     q: [B, Sq, H, D]; k_blocks[j], v_blocks[j]: [B, Ck_j, H, D]; block j holds
-    global key positions kv_pos0s[j] + 0..Ck_j-1; query row r sits at global
-    position q_pos0 + r.  The ring schedule of "Ring Attention: Partition
-    Sequence Length, Not Batch" (tildalice page) delivers every block exactly
-    once, so the union of the blocks is the key set.
+    global key positions kv_pos0s[j] + i * pos_stride for i = 0..Ck_j-1; query
+    row r sits at global position q_pos0 + r * pos_stride.  pos_stride 1 is a
+    contiguous chunk; pos_stride P the striped order (device i of P holds
+    tokens i, i+P, ...), a reading of the Striped Attention entry of section
+    "How Does This Compare to Other Long-Context Methods?" of "Ring Attention:
+    Train 1M Tokens on 8GB GPUs in 2026".  The ring schedule of that page's
+    section "Ring Attention: Partition Sequence Length, Not Batch" delivers
+    every block exactly once, so the union of the blocks is the key set.
+    Blocks may have different lengths (chunks of unequal length, the same
+    page's FAQ).
 
     rows / heads restrict the evaluation to sampled query rows / heads.
     Returns (O [B, R, Hs, D], LSE [B, Hs, R]) in float64.
@@ -115,12 +123,12 @@ def ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int,
         scale = default_scale(d)
     rows = np.arange(sq) if rows is None else np.asarray(rows, dtype=np.int64)
     heads = list(range(nh)) if heads is None else list(heads)
-    ks, vs, ps = _gather_blocks(k_blocks, v_blocks, kv_pos0s)
+    ks, vs, ps = _gather_blocks(k_blocks, v_blocks, kv_pos0s, pos_stride)
     kv_pos = np.concatenate(ps) if ps else np.zeros((0,), np.int64)
     dv = vs[0].shape[3] if vs else d
     out = np.zeros((bsz, rows.shape[0], len(heads), dv))
     lse = np.full((bsz, len(heads), rows.shape[0]), -np.inf)
-    q_pos = int(q_pos0) + rows
+    q_pos = int(q_pos0) + int(pos_stride) * rows
     for b in range(bsz):
         for hi, h in enumerate(heads):
             qh = np.asarray(q[b, rows, h, :], dtype=np.float64)
@@ -137,12 +145,13 @@ def ring_attention(q, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int,
 
 
 def partial_state(q, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int,
-                  kv_pos0s: Sequence[int], causal: bool, scale: float | None = None):
+                  kv_pos0s: Sequence[int], causal: bool, scale: float | None = None, pos_stride: int = 1):
     """The (m, l, acc) triple after a device has processed the given blocks.
 
     Closed form of the state named in the "Gotchas and Failure Modes" section
-    of the tildalice page (running max, running sum, weighted output), over
-    the visible keys of the processed blocks S:
+    of "Ring Attention: Train 1M Tokens on 8GB GPUs in 2026" (running max,
+    running sum, weighted output), over the visible keys of the processed
+    blocks S (positions as in ring_attention):
       m   = max_{j in S} s_j                     (natural-log score units)
       l   = sum_{j in S} exp(s_j - m)
       acc = sum_{j in S} exp(s_j - m) v_j        (unnormalised output)
@@ -154,7 +163,7 @@ def partial_state(q, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int,
     bsz, sq, nh, d = q.shape
     if scale is None:
         scale = default_scale(d)
-    ks, vs, ps = _gather_blocks(k_blocks, v_blocks, kv_pos0s)
+    ks, vs, ps = _gather_blocks(k_blocks, v_blocks, kv_pos0s, pos_stride)
     dv = vs[0].shape[3] if vs else d
     m = np.full((bsz, nh, sq), -np.inf)
     l = np.zeros((bsz, nh, sq))
@@ -162,7 +171,7 @@ def partial_state(q, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int,
     if not ks:
         return m, l, acc
     kv_pos = np.concatenate(ps)
-    vis = visible(int(q_pos0) + np.arange(sq), kv_pos, causal)
+    vis = visible(int(q_pos0) + int(pos_stride) * np.arange(sq), kv_pos, causal)
     has = vis.any(axis=1)
     for b in range(bsz):
         for h in range(nh):

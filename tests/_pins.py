@@ -215,7 +215,33 @@ def pin_partial_state(orc):
         assert np.allclose(fa[..., None] * aa + fb[..., None] * ab, acc, rtol=0, atol=1e-12)
 
 
+def pin_striped_is_permuted_contiguous(orc):
+    """Striped order (pos_stride P): device i holds tokens i, i+P, ... of the
+    sequence and block d holds keys d, d+P, ...  Its causal attention must be
+    the rows i, i+P, ... of the attention of the whole sequence in natural
+    order (one contiguous chunk and block).  The final state of partial_state
+    over every block must give the same output and LSE."""
+    p, n, h, d = 4, 5, 2, 3
+    rng = np.random.default_rng(23)
+    q = rng.standard_normal((1, p * n, h, d))
+    k = rng.standard_normal((1, p * n, h, d))
+    v = rng.standard_normal((1, p * n, h, d))
+    o_full, lse_full = orc.ring_attention(q, [k], [v], 0, [0], True)
+    for i in range(p):
+        qi = q[:, i::p]
+        kbs = [k[:, dd::p] for dd in range(p)]
+        vbs = [v[:, dd::p] for dd in range(p)]
+        o, lse = orc.ring_attention(qi, kbs, vbs, i, list(range(p)), True, pos_stride=p)
+        assert np.allclose(o, o_full[:, i::p], rtol=0, atol=1e-12)
+        assert np.allclose(lse, lse_full[:, :, i::p], rtol=0, atol=1e-12)
+        m, l, acc = orc.partial_state(qi, kbs, vbs, i, list(range(p)), True, pos_stride=p)
+        o_st = np.transpose(acc / l[..., None], (0, 2, 1, 3))
+        assert np.allclose(o_st, o, rtol=0, atol=1e-12)
+        assert np.allclose(m + np.log(l), lse, rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
+    pin_striped_is_permuted_contiguous,
     pin_mpmath_bruteforce,
     pin_single_visible_key,
     pin_identical_keys,

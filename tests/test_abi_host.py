@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = ra.lib()
-    assert L.ringattn_abi_version() == 1
+    assert L.ringattn_abi_version() == ra.ABI_VERSION == 2
     for st in range(8):
         assert L.ringattn_status_str(st).startswith(b"RA_")
 
@@ -57,6 +57,7 @@ def _desc(**kw):
     d.scale = kw.get("scale", 0.0)
     d.in_dtype, d.out_dtype = kw.get("in_dtype", ra.RA_BF16), kw.get("out_dtype", ra.RA_BF16)
     d.flags = kw.get("flags", 0)
+    d.pos_stride = kw.get("pos_stride", 1)
     hd = d.heads * d.head_dim
     for arr, s in ((d.q_stride, kw.get("q_stride")), (d.kv_stride, kw.get("kv_stride")),
                    (d.o_stride, kw.get("o_stride"))):
@@ -86,17 +87,18 @@ FAKE = 1 << 20  # aligned, never dereferenced: validation fails before any acces
 
 
 def _ring(d, q=FAKE, o=FAKE, lse=FAKE, kb=(FAKE,), vb=(FAKE,), pos=(0,), on_host=0, stage=None, m=None,
-          l=None, acc=None, copy=None, compute=None):
+          l=None, acc=None, copy=None, compute=None, valid=None):
     L = ra.lib()
     P = ctypes.c_void_p
     n = len(kb) if kb is not None else len(vb)
     karr = (P * max(n, 1))(*kb) if kb is not None else None
     varr = (P * max(n, 1))(*vb) if vb is not None else None
     parr = (ctypes.c_int64 * max(n, 1))(*pos)
+    varr_len = (ctypes.c_int64 * max(n, 1))(*valid) if valid is not None else None
     sk = (P * 2)(*stage) if stage else None
     sv = (P * 2)(*stage) if stage else None
-    st = L.ringattn_ring_fwd(ctypes.byref(d) if d is not None else None, q, karr, varr, parr, n, on_host, sk, sv,
-                             m, l, acc, o, lse, compute, copy)
+    st = L.ringattn_ring_fwd(ctypes.byref(d) if d is not None else None, q, karr, varr, parr, varr_len, n, on_host,
+                             sk, sv, m, l, acc, o, lse, compute, copy)
     return st, L.ringattn_last_error().decode()
 
 
@@ -117,6 +119,7 @@ def _ring(d, q=FAKE, o=FAKE, lse=FAKE, kb=(FAKE,), vb=(FAKE,), pos=(0,), on_host
     (dict(kv_len=1 << 30, kv_stride=(128, 128, 128)), ra.RA_E_UNSUPPORTED),  # keys per block must be < 2^30
     (dict(kv_stride=(256 * 256, 64, 128)), ra.RA_E_SHAPE),   # key rows overlap (stride < head_dim)
     (dict(flags=4), ra.RA_E_UNSUPPORTED),
+    (dict(pos_stride=-1), ra.RA_E_SHAPE),
 ])
 def test_descriptor_rejected_before_enqueue(kw, status):
     st, msg = _ring(_desc(**kw))
@@ -150,3 +153,33 @@ def test_valid_call_without_device_reports_hip_error():
     st, msg = _ring(_desc())
     assert st in (ra.RA_E_HIP, ra.RA_E_MEMTYPE), (st, msg)
     assert msg
+
+
+@pytest.mark.parametrize("valid", [(-1,), (257,)])
+def test_valid_length_out_of_range_rejected(valid):
+    """kv_valid[i] must lie in [0, kv_len]; checked before anything is enqueued."""
+    st, msg = _ring(_desc(kv_len=256), valid=valid)
+    assert st == ra.RA_E_SHAPE and "kv_valid" in msg, (st, msg)
+
+
+def _floor_div(a, b):
+    return a // b  # Python floors
+
+
+@pytest.mark.parametrize("p,i", [(4, 0), (4, 3), (8, 5)])
+def test_block_class_striped_matches_brute_force(p, i):
+    """With pos_stride P (striped order), the class of block d follows from the
+    visibility of key j*P + d to row r*P + i, enumerated directly."""
+    n = 8
+    d = _desc(q_len=n, kv_len=n, q_pos0=i, pos_stride=p, q_stride=(n * 256, 256, 128),
+              kv_stride=(n * 256, 256, 128), o_stride=(n * 256, 256, 128))
+    for dev in range(p):
+        vis = [[j * p + dev <= r * p + i for j in range(n)] for r in range(n)]
+        flat = [x for row in vis for x in row]
+        want = ra.RA_BLOCK_FULL if all(flat) else (ra.RA_BLOCK_SKIP if not any(flat) else ra.RA_BLOCK_DIAG)
+        assert ra.ringattn_block_class(d, dev) == want, (dev, p, i)
+    # a block placed far after the chunk (key 0 after the last row) is skipped
+    assert ra.ringattn_block_class(d, (n - 1) * p + i + 1) == ra.RA_BLOCK_SKIP
+    d.pos_stride = -2
+    assert ra.ringattn_block_class(d, 0) == -1
+

@@ -1,5 +1,6 @@
 """The fp32 gate (max-abs 1e-5) must tell the exact online-softmax merge from the
-per-chunk merge printed in the tildalice page's PyTorch section, which weights
+per-chunk merge printed in the PyTorch section of "Ring Attention: Train 1M
+Tokens on 8GB GPUs in 2026", which weights
 each chunk's softmax output by that chunk's exp-sum taken against the chunk's
 own maximum and never brings the chunks to a common maximum."""
 

@@ -21,9 +21,13 @@ MUTANTS = {
     "wrong_operand": ("out[has] = (e @ v) / l", "out[has] = (e @ k[:, :v.shape[1]]) / l"),
     "no_normalise": ("out[has] = (e @ v) / l", "out[has] = (e @ v)"),
     "block_positions": ("ps.append(int(kv_pos0s[j])", "ps.append(int(kv_pos0s[0])"),
-    "local_positions": ("q_pos = int(q_pos0) + rows", "q_pos = rows"),
+    "local_positions": ("q_pos = int(q_pos0) + int(pos_stride) * rows", "q_pos = int(pos_stride) * rows"),
     "state_normalised": ("acc[b, h, has, :] = e @ vh", "acc[b, h, has, :] = (e @ vh) / e.sum(axis=1)[:, None]"),
     "state_log2": ("m[b, h, has] = mh", "m[b, h, has] = mh / 0.6931471805599453"),
+    "stride_kv_ignored": ("int(pos_stride) * np.arange(kb.shape[1]", "np.arange(kb.shape[1]"),
+    "stride_q_ignored": ("q_pos = int(q_pos0) + int(pos_stride) * rows", "q_pos = int(q_pos0) + rows"),
+    "state_stride_ignored": ("visible(int(q_pos0) + int(pos_stride) * np.arange(sq)",
+                             "visible(int(q_pos0) + np.arange(sq)"),
 }
 
 
