@@ -25,6 +25,11 @@ What it computes, and from which passage:
   processed so far (not as an iteration), following the online-normaliser idea
   of Milakov & Gimelshein cited in the arXiv record's reference list.
 
+* ``ring_attention_bwd`` / ``delta`` (``backward.py``): the exact gradients of
+  that output with respect to Q, K and V for an upstream dO (the pages train
+  through the ring but never write the backward pass; the reading is stated
+  in that module).
+
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 brute force in 50-digit arithmetic, closed forms, invariants and a library
 routine.  No function here is "parity unpinned".
@@ -37,3 +42,4 @@ from .attention import (  # noqa: F401
     ring_attention,
     visible,
 )
+from .backward import delta, ring_attention_bwd  # noqa: F401
