@@ -178,6 +178,38 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
                             int32_t kv_on_host, void* const* stage_k, void* const* stage_v, float* m, float* l,
                             float* acc, void* o, float* lse, hipStream_t compute, hipStream_t copy);
 
+/* ---- Backward pass (bf16 inputs only; F32 descriptors give RA_E_UNSUPPORTED).
+ * The exact gradient of the output above, the reading taken because the
+ * pages train through the ring ("Ring Attention: Train 1M Tokens on 8GB GPUs
+ * in 2026", sections "Training Speed: The Numbers" and "Gotchas and Failure
+ * Modes") without writing the backward out.  dout (the upstream gradient of
+ * O) has Q's layout, strides and dtype; lse is the forward's LSE.  dq is
+ * [B, Sq, H, D] and each block's dk, dv [B, kv_len, H, D], fp32, contiguous.
+ * A device computes dQ of its chunk and, for every block it receives, its
+ * contribution to that block's dK and dV, which in the ring travel on with
+ * the block and add up across devices. */
+
+/* delta[b, h, r] = sum_d dout[b, r, h, d] * o[b, r, h, d] (fp32 [B, H, Sq]; o in
+ * out_dtype with o_stride). */
+ra_status ringattn_bwd_delta(const ra_desc* desc, const void* o, const void* dout, float* delta, hipStream_t stream);
+
+/* One block: dq += this block's part of dQ; dk += and dv += this chunk's
+ * contribution (the block's kv_len keys at kv_pos0 + j*pos_stride).  A block
+ * with no key visible to any row enqueues nothing and returns RA_OK. */
+ra_status ringattn_block_bwd(const ra_desc* desc, const void* q, const void* k, const void* v, int64_t kv_pos0,
+                             const void* dout, const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                             hipStream_t stream);
+
+/* Whole ring backward on `stream`: delta (into the caller's [B, H, Sq] fp32
+ * workspace), dq = 0, then block_bwd for every block (kv_valid as in
+ * ringattn_ring_fwd).  dk_blocks[i] and dv_blocks[i] are accumulated into
+ * (+=): zero them for the first device of the ring.  Host arrays: k_blocks,
+ * v_blocks, kv_pos0, kv_valid, dk_blocks, dv_blocks. */
+ra_status ringattn_ring_bwd(const ra_desc* desc, const void* q, const void* const* k_blocks,
+                            const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
+                            int32_t num_blocks, const void* o, const void* dout, const float* lse, float* delta,
+                            float* dq, float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream);
+
 /* Measurement helper, not part of the attention path: a plain device-to-device
  * copy kernel of `bytes` (multiple of 16, 16-byte aligned pointers), used to
  * calibrate hardware byte counters and HBM bandwidth. */

@@ -1,0 +1,94 @@
+// Device helpers shared by the bf16 attention kernels (forward and backward),
+// gfx950.  Included by the kernel translation units only.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace ra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Row-major placement of 16-byte chunk c of key row `key` in a tile.  K rows
+// are read 16 bytes per lane, 16 rows at a time at one chunk column: XOR the
+// column with the row so those 16 reads hit 16 different 16-byte bank groups.
+// V rows are read by the transpose loads 8 rows x 4 chunks at a time: XOR the
+// 4-chunk group with the row so the 8 rows spread over the banks.
+template <int D>
+__device__ __forceinline__ int k_off(int key, int c) {
+  const int cs = (D == 128) ? (c ^ (key & 15)) : (c ^ ((key >> 1) & 7));
+  return key * (D * 2) + cs * 16;
+}
+template <int D>
+__device__ __forceinline__ int v_off(int key, int c) {
+  const int cs = (D == 128) ? (c ^ ((key & 3) << 2)) : (c ^ (((key >> 1) & 1) << 2));
+  return key * (D * 2) + cs * 16;
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  // max(x[lane], x[lane ^ 32]) on every lane
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// i's bytes land at LDS byte lds_addr + 16 i.  base and lds_addr are
+// wave-uniform.  The copies are issued from inline assembly so that the
+// compiler does not track them: its own tracking would wait for every copy in
+// flight before the next LDS read of any buffer, which serialises the prefetch
+// with the compute.  The kernel waits for its copies itself (s_waitcnt
+// vmcnt) before the barrier that publishes a buffer.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
+  // (readfirstlane returns int: widen through uint32_t, never by sign extension)
+  const uint64_t bv = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
+// LDS byte address of a generic pointer into the dynamic LDS array.
+__device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without a memory fence: every wait a barrier needs here
+// is explicit (the copies' vmcnt; LDS reads are consumed before the barrier).
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace
+}  // namespace ra

@@ -42,6 +42,28 @@ struct AttnArgs {
   int32_t out_bf16;   // 1: O is bf16, 0: fp32
 };
 
+// One block of the backward pass (bf16 inputs).  Positions are in row units
+// (contiguous-equivalent, see the API layer).  dout has q's layout; lse and
+// delta are [B, H, Sq] fp32; dq is [B, Sq, H, D] and dk, dv are [B, kv_len, H, D],
+// fp32, contiguous, accumulated into (+=).
+struct BwdArgs {
+  const void* q;
+  const void* dout;
+  const void* k;
+  const void* v;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int64_t q_sb, q_ss, q_sh;
+  int64_t kv_sb, kv_ss, kv_sh;
+  int64_t q_len, kv_len, q_pos0, kv_pos0;  // kv_len: the block's valid keys; dk/dv rows are kv_cap
+  int64_t kv_cap;                          // key capacity of the block (rows of dk, dv)
+  int32_t batch, heads, head_dim, causal;
+  float scale;
+};
+
 // Launchers: validate nothing (the API layer did), enqueue, return the launch
 // error (hipSuccess on success).
 hipError_t launch_attn_bf16(const AttnArgs& a, const BlockTable& t, int mode, hipStream_t s);
@@ -49,5 +71,9 @@ hipError_t launch_attn_f32(const AttnArgs& a, const BlockTable& t, int mode, hip
 hipError_t launch_init_state(int64_t rows, int32_t d, float* m, float* l, float* acc, hipStream_t s);
 hipError_t launch_finalize(const AttnArgs& a, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+// delta[b, h, r] = sum_d dout[b, r, h, d] * o[b, r, h, d]
+hipError_t launch_bwd_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t s);
+hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s);
+hipError_t launch_fill(float* p, int64_t n, hipStream_t s);
 
 }  // namespace ra

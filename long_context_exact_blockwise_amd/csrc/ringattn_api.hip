@@ -17,6 +17,7 @@ namespace {
 
 using ra::AttnArgs;
 using ra::BlockTable;
+using ra::BwdArgs;
 
 thread_local std::string g_err;
 
@@ -200,6 +201,51 @@ hipError_t events_ready() {
   return hipSuccess;
 }
 
+}  // namespace
+
+// ---- backward helpers ----
+
+namespace {
+ra_status check_bwd_desc(const ra_desc* d) {
+  ra_status st;
+  if ((st = check_desc(d)) != RA_OK) return st;
+  if (d->in_dtype != RA_BF16) return fail(RA_E_UNSUPPORTED, "the backward pass takes bf16 inputs");
+  if (d->q_stride[1] * 2 * 64 >= (int64_t)1 << 31)
+    return fail(RA_E_UNSUPPORTED, "q_stride[1] too large (a 64-row tile must span < 2 GiB)");
+  return RA_OK;
+}
+
+BwdArgs make_bwd(const ra_desc* d, const void* q, const void* k, const void* v, int64_t kv_pos0, int64_t valid,
+                 const void* dout, const float* lse, const float* delta, float* dq, float* dk, float* dv) {
+  BwdArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q;
+  a.dout = dout;
+  a.k = k;
+  a.v = v;
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.q_sb = d->q_stride[0];
+  a.q_ss = d->q_stride[1];
+  a.q_sh = d->q_stride[2];
+  a.kv_sb = d->kv_stride[0];
+  a.kv_ss = d->kv_stride[1];
+  a.kv_sh = d->kv_stride[2];
+  a.q_len = d->q_len;
+  a.kv_len = valid;
+  a.kv_cap = d->kv_len;
+  a.q_pos0 = q_pos_eff(d);
+  a.kv_pos0 = kv_pos_eff(d, kv_pos0);
+  a.batch = d->batch;
+  a.heads = d->heads;
+  a.head_dim = d->head_dim;
+  a.causal = d->causal;
+  a.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
+  return a;
+}
 }  // namespace
 
 extern "C" {
@@ -431,6 +477,90 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
   }
   e = ra::launch_finalize(a, compute);
   return e == hipSuccess ? RA_OK : hip_fail(e, "finalize launch");
+}
+
+
+ra_status ringattn_bwd_delta(const ra_desc* desc, const void* o, const void* dout, float* delta, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_bwd_desc(desc)) != RA_OK) return st;
+  if (desc->q_len == 0) return RA_OK;
+  const void* ptrs[] = {o, dout, delta};
+  const char* names[] = {"o", "dout", "delta"};
+  for (int i = 0; i < 3; ++i)
+    if ((st = need_ptr(ptrs[i], names[i])) != RA_OK) return st;
+  for (int i = 0; i < 3; ++i)
+    if ((st = check_mem(ptrs[i], false, names[i])) != RA_OK) return st;
+  AttnArgs a = make_args(desc, nullptr, (void*)o, nullptr, nullptr, nullptr, nullptr);
+  hipError_t e = ra::launch_bwd_delta(a, dout, delta, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "delta launch");
+}
+
+ra_status ringattn_block_bwd(const ra_desc* desc, const void* q, const void* k, const void* v, int64_t kv_pos0,
+                             const void* dout, const float* lse, const float* delta, float* dq, float* dk, float* dv,
+                             hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_bwd_desc(desc)) != RA_OK) return st;
+  if (desc->q_len == 0 || desc->kv_len == 0) return RA_OK;
+  const void* ptrs[] = {q, k, v, dout, lse, delta, dq, dk, dv};
+  const char* names[] = {"q", "k", "v", "dout", "lse", "delta", "dq", "dk", "dv"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = need_ptr(ptrs[i], names[i])) != RA_OK) return st;
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_mem(ptrs[i], false, names[i])) != RA_OK) return st;
+  if (classify(desc, kv_pos0, desc->kv_len) == RA_BLOCK_SKIP) return RA_OK;
+  BwdArgs a = make_bwd(desc, q, k, v, kv_pos0, desc->kv_len, dout, lse, delta, dq, dk, dv);
+  hipError_t e = ra::launch_bwd_block(a, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "backward block launch");
+}
+
+ra_status ringattn_ring_bwd(const ra_desc* desc, const void* q, const void* const* k_blocks,
+                            const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
+                            int32_t num_blocks, const void* o, const void* dout, const float* lse, float* delta,
+                            float* dq, float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = check_bwd_desc(desc)) != RA_OK) return st;
+  if (num_blocks < 0) return fail(RA_E_SHAPE, "num_blocks must be >= 0");
+  if (desc->q_len == 0) return RA_OK;
+  if (num_blocks > 0 && (!k_blocks || !v_blocks || !kv_pos0 || !dk_blocks || !dv_blocks))
+    return fail(RA_E_NULL, "k_blocks, v_blocks, kv_pos0, dk_blocks and dv_blocks are required when num_blocks > 0");
+  const void* ptrs[] = {q, o, dout, lse, delta, dq};
+  const char* names[] = {"q", "o", "dout", "lse", "delta", "dq"};
+  for (int i = 0; i < 6; ++i)
+    if ((st = need_ptr(ptrs[i], names[i])) != RA_OK) return st;
+  auto valid = [&](int i) -> int64_t { return kv_valid ? kv_valid[i] : desc->kv_len; };
+  for (int i = 0; i < num_blocks; ++i) {
+    if ((st = need_ptr(k_blocks[i], "k_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(v_blocks[i], "v_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(dk_blocks[i], "dk_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(dv_blocks[i], "dv_blocks[i]")) != RA_OK) return st;
+    if (valid(i) < 0 || valid(i) > desc->kv_len)
+      return fail(RA_E_SHAPE, "kv_valid[%d] = %lld must be in [0, kv_len = %lld]", i, (long long)valid(i),
+                  (long long)desc->kv_len);
+  }
+  for (int i = 0; i < 6; ++i)
+    if ((st = check_mem(ptrs[i], false, names[i])) != RA_OK) return st;
+  for (int i = 0; i < num_blocks; ++i) {
+    if ((st = check_mem(k_blocks[i], false, "k_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(v_blocks[i], false, "v_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(dk_blocks[i], false, "dk_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(dv_blocks[i], false, "dv_blocks[i]")) != RA_OK) return st;
+  }
+  AttnArgs da = make_args(desc, nullptr, (void*)o, nullptr, nullptr, nullptr, nullptr);
+  hipError_t e = ra::launch_bwd_delta(da, dout, delta, stream);
+  if (e != hipSuccess) return hip_fail(e, "delta launch");
+  e = ra::launch_fill(dq, (int64_t)desc->batch * desc->q_len * desc->heads * desc->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  for (int i = 0; i < num_blocks; ++i) {
+    if (classify(desc, kv_pos0[i], valid(i)) == RA_BLOCK_SKIP) continue;
+    BwdArgs a = make_bwd(desc, q, k_blocks[i], v_blocks[i], kv_pos0[i], valid(i), dout, lse, delta, dq,
+                         dk_blocks[i], dv_blocks[i]);
+    e = ra::launch_bwd_block(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward block launch");
+  }
+  return RA_OK;
 }
 
 ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {

@@ -61,6 +61,37 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(const u32x4* __restrict_
     dst[i] = src[i];
 }
 
+// Backward preprocessing: delta[row] = sum_d dO[row, d] O[row, d] (rows in
+// state order (b, h, r)).  D/8 consecutive lanes share a row, 8 elements
+// (16 bytes of dO) each, and reduce with lane swaps.
+template <typename OutT>
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(AttnArgs a, const __bf16* __restrict__ dout,
+                                                             float* __restrict__ delta) {
+  const int tpr = a.head_dim / 8;
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t row = g / tpr;
+  const int part = (int)(g - row * tpr);
+  const int64_t nrow = (int64_t)a.batch * a.heads * a.q_len;
+  float sum = 0.f;
+  if (row < nrow) {
+    const int64_t bh = row / a.q_len;
+    const int64_t r = row - bh * a.q_len;
+    const int64_t b = bh / a.heads;
+    const int64_t h = bh - b * a.heads;
+    const __bf16* dp = dout + b * a.q_sb + r * a.q_ss + h * a.q_sh + 8 * part;
+    const OutT* op = (const OutT*)a.o + b * a.o_sb + r * a.o_ss + h * a.o_sh + 8 * part;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += (float)dp[j] * (float)op[j];
+  }
+  for (int m = 1; m < tpr; m <<= 1) sum += __shfl_xor(sum, m);
+  if (row < nrow && part == 0) delta[row] = sum;
+}
+
+__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    p[i] = 0.f;
+}
+
 unsigned grid_for(int64_t n) {
   int64_t g = (n + kThreads - 1) / kThreads;
   const int64_t cap = 256 * 16;  // 16 workgroups per CU, grid-stride beyond
@@ -90,6 +121,23 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s)
   const int64_t n = bytes / 16;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, (const u32x4*)src, (u32x4*)dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t s) {
+  const int64_t n = (int64_t)a.batch * a.heads * a.q_len * (a.head_dim / 8);
+  if (n == 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
+  if (a.out_bf16)
+    hipLaunchKernelGGL(bwd_delta_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, a, (const __bf16*)dout, delta);
+  else
+    hipLaunchKernelGGL(bwd_delta_kernel<float>, dim3(grid), dim3(kThreads), 0, s, a, (const __bf16*)dout, delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, p, n);
   return hipGetLastError();
 }
 

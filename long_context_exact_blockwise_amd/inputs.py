@@ -106,6 +106,15 @@ def make_inputs(wl: Workload, device="cpu", seed: int = 0, q_mult: float = 1.0,
     return Inputs(wl, q.to(dt), k.to(dt), v.to(dt))
 
 
+def make_grad(wl: Workload, device="cpu", seed: int = 0) -> torch.Tensor:
+    """Upstream gradient dO for the backward pass: fp32 randn in Q's shape
+    [B, Sq, H, D] from its own seeded generator, rounded to the input dtype."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    do = torch.randn((wl.batch, wl.q_len, wl.heads, wl.head_dim), generator=g, device=device, dtype=torch.float32)
+    return do.to(torch_dtype(wl.dtype))
+
+
 def sample_rows(q_len: int, extra: int = 8, seed: int = 1):
     """Rows checked at full size: the first, the last and `extra` seeded rows."""
     import numpy as np

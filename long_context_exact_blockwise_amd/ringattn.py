@@ -29,7 +29,7 @@ ABI_VERSION = 2
 SYMBOLS = (
     "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
     "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
-    "ringattn_ring_fwd", "ringattn_probe_copy",
+    "ringattn_ring_fwd", "ringattn_probe_copy", "ringattn_bwd_delta", "ringattn_block_bwd", "ringattn_ring_bwd",
 )
 
 
@@ -84,6 +84,14 @@ def lib():
                                     ctypes.POINTER(P), ctypes.POINTER(P), P, P, P, P, P, P, P]
     L.ringattn_probe_copy.restype = ctypes.c_int
     L.ringattn_probe_copy.argtypes = [P, P, ctypes.c_int64, P]
+    L.ringattn_bwd_delta.restype = ctypes.c_int
+    L.ringattn_bwd_delta.argtypes = [D, P, P, P, P]
+    L.ringattn_block_bwd.restype = ctypes.c_int
+    L.ringattn_block_bwd.argtypes = [D, P, P, P, ctypes.c_int64, P, P, P, P, P, P, P]
+    L.ringattn_ring_bwd.restype = ctypes.c_int
+    L.ringattn_ring_bwd.argtypes = [D, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(ctypes.c_int64),
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P, P, P, P,
+                                    ctypes.POINTER(P), ctypes.POINTER(P), P]
     if L.ringattn_abi_version() != ABI_VERSION:
         raise RuntimeError("libringattn.so ABI version mismatch")
     _lib = L
@@ -228,3 +236,49 @@ def ring_forward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: Se
 
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+# ---- backward ----
+
+def ringattn_bwd_delta(desc: RaDesc, o, dout, delta, stream=None):
+    _check(lib().ringattn_bwd_delta(ctypes.byref(desc), _ptr(o), _ptr(dout), _ptr(delta), _stream(stream)))
+
+
+def ringattn_block_bwd(desc: RaDesc, q, k, v, kv_pos0: int, dout, lse, delta, dq, dk, dv, stream=None):
+    _check(lib().ringattn_block_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), kv_pos0, _ptr(dout), _ptr(lse),
+                                    _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)))
+
+
+def ringattn_ring_bwd(desc: RaDesc, q, k_blocks: Sequence, v_blocks: Sequence, kv_pos0: Sequence[int], o, dout, lse,
+                      delta, dq, dk_blocks: Sequence, dv_blocks: Sequence, *, kv_valid: Optional[Sequence[int]] = None,
+                      stream=None):
+    n = len(k_blocks)
+    P = ctypes.c_void_p
+    arr = lambda ts: (P * max(n, 1))(*[t.data_ptr() for t in ts])  # noqa: E731
+    pp = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_pos0])
+    nv = None if kv_valid is None else (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_valid])
+    _check(lib().ringattn_ring_bwd(ctypes.byref(desc), _ptr(q), arr(k_blocks), arr(v_blocks), pp, nv, n, _ptr(o),
+                                   _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), arr(dk_blocks), arr(dv_blocks),
+                                   _stream(stream)))
+
+
+def ring_backward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: Sequence[torch.Tensor],
+                  kv_pos0: Sequence[int], o: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor, *, q_pos0: int = 0,
+                  causal: bool = False, scale: float = 0.0, kv_valid: Optional[Sequence[int]] = None,
+                  pos_stride: int = 1):
+    """Gradients of one device's ring-attention output (bf16 inputs).  Returns
+    (dQ, [dK_i], [dV_i]) fp32 in [B, S, H, D]; dK_i / dV_i are this chunk's
+    contributions to block i (allocated zeroed here)."""
+    b, sq, h, d = q.shape
+    desc = make_desc(q, k_blocks[0] if len(k_blocks) else q, o, q_pos0=q_pos0, causal=causal, scale=scale,
+                     pos_stride=pos_stride)
+    if len(k_blocks) == 0:
+        desc.kv_len = 0
+    ck = desc.kv_len
+    delta = torch.empty((b, h, sq), dtype=torch.float32, device=q.device)
+    dq = torch.empty((b, sq, h, d), dtype=torch.float32, device=q.device)
+    dk = [torch.zeros((b, ck, h, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
+    dv = [torch.zeros((b, ck, h, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
+    ringattn_ring_bwd(desc, q, k_blocks, v_blocks, kv_pos0, o, dout, lse, delta, dq, dk, dv, kv_valid=kv_valid)
+    return dq, dk, dv
+

@@ -183,3 +183,36 @@ def test_block_class_striped_matches_brute_force(p, i):
     d.pos_stride = -2
     assert ra.ringattn_block_class(d, 0) == -1
 
+
+
+def _ring_bwd(d, kb=(FAKE,), pos=(0,), valid=None, n=None, dk=(FAKE,), q=FAKE):
+    L = ra.lib()
+    P = ctypes.c_void_p
+    n = len(kb) if n is None else n
+    arr = lambda xs: (P * max(len(xs), 1))(*xs) if xs is not None else None  # noqa: E731
+    parr = (ctypes.c_int64 * max(len(pos), 1))(*pos)
+    varr = (ctypes.c_int64 * max(len(pos), 1))(*valid) if valid is not None else None
+    st = L.ringattn_ring_bwd(ctypes.byref(d), q, arr(kb), arr(kb), parr, varr, n, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             arr(dk), arr(dk), None)
+    return st, L.ringattn_last_error().decode()
+
+
+def test_backward_checks_before_enqueue():
+    """The backward entry points validate like the forward and take bf16
+    inputs only."""
+    L = ra.lib()
+    st, msg = _ring_bwd(_desc(in_dtype=ra.RA_F32, out_dtype=ra.RA_F32))
+    assert st == ra.RA_E_UNSUPPORTED and "bf16" in msg, (st, msg)
+    assert _ring_bwd(_desc(head_dim=96))[0] == ra.RA_E_UNSUPPORTED
+    assert _ring_bwd(_desc(), n=-1)[0] == ra.RA_E_SHAPE
+    assert _ring_bwd(_desc(), q=None)[0] == ra.RA_E_NULL
+    assert _ring_bwd(_desc(), dk=None)[0] == ra.RA_E_NULL
+    assert _ring_bwd(_desc(), dk=(FAKE + 4,))[0] == ra.RA_E_ALIGN
+    st, msg = _ring_bwd(_desc(kv_len=256), valid=(300,))
+    assert st == ra.RA_E_SHAPE and "kv_valid" in msg
+    d = _desc()
+    assert L.ringattn_block_bwd(ctypes.byref(d), FAKE, FAKE, None, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                None) == ra.RA_E_NULL
+    assert L.ringattn_bwd_delta(ctypes.byref(d), FAKE, FAKE, FAKE + 2, None) == ra.RA_E_ALIGN
+    d32 = _desc(in_dtype=ra.RA_F32, out_dtype=ra.RA_F32)
+    assert L.ringattn_bwd_delta(ctypes.byref(d32), FAKE, FAKE, FAKE, None) == ra.RA_E_UNSUPPORTED
