@@ -7,6 +7,13 @@ HBM before timing starts.  Default workload: 16 heads, head_dim 128, local
 query chunk 131072 rows (512K tokens over a ring of 4), 4 KV blocks of 131072
 keys, causal with the chunk at ring index 3, bf16 in / fp32 accumulate.
 
+Unless --no-backward, the same line carries a `backward` object: the
+gradient pass through the ring (delta, dQ of the chunk and the chunk's dK/dV
+contribution for every block) timed on the same inputs with the forward's O
+and LSE, in algorithmic TFLOP/s (10*B*H*D*(visible pairs): the five products
+S, dP, dQ, dK, dV), with dQ checked against the oracle on sampled rows and the
+sums of dK and dV over all keys checked against their closed forms.
+
 Prints ONE JSON line.  `value` is causal-adjusted TFLOP/s: 4*B*H*D*(visible
 query-key pairs) per step over the measured step time.  `roofline` prices the
 fused attention kernel's live-measured duration (HIP events on the launch
@@ -14,7 +21,7 @@ stream) against the bf16 dense MFMA peak.  `cpu_baseline` times the fp64 CPU
 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
-       [--perblock] [--no-cpu-baseline] [--traffic-calib]
+       [--perblock] [--no-cpu-baseline] [--traffic-calib] [--no-backward] [--bwd-steps K]
 """
 
 from __future__ import annotations
@@ -32,7 +39,8 @@ sys.path.insert(0, ROOT)
 METRIC = "causal-adjusted attention TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 dense bf16 flop/clk/CU x 2.4 GHz (AMD's published 2.5 PF)
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "long_context_exact_blockwise_amd", "csrc", "attn_bf16.hip")
+KERNEL_SRC = [os.path.join(ROOT, "long_context_exact_blockwise_amd", "csrc", f)
+              for f in ("attn_bf16.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_fused_causal_q131072_p4_traffic.txt")
 
 
@@ -65,8 +73,11 @@ def flops(wl) -> int:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():
@@ -84,6 +95,85 @@ def read_traffic():
         return int(float(kv["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
         return None
+
+
+def bwd_flops(wl) -> int:
+    return 10 * wl.batch * wl.heads * wl.head_dim * visible_pairs(wl)
+
+
+def backward_measure(x, wl, kb, vb, pos, o, lse, steps, warmup, sample_heads):
+    """Time the ring backward and check it at full size: dQ on sampled rows
+    against the oracle; sum_c dK_c = 0 and sum_c dV_c = sum_r dO_r (every row
+    sees a key) per head, in fp64 on the host."""
+    import numpy as np
+    import torch
+    import oracle
+    from long_context_exact_blockwise_amd import inputs
+    from long_context_exact_blockwise_amd import ringattn as ra
+    dev = x.q.device
+    do = inputs.make_grad(wl, dev, seed=1)
+    desc = ra.make_desc(x.q, kb[0], o, q_pos0=wl.q_pos0, causal=wl.causal)
+    delta = torch.empty((wl.batch, wl.heads, wl.q_len), dtype=torch.float32, device=dev)
+    dq = torch.empty((wl.batch, wl.q_len, wl.heads, wl.head_dim), dtype=torch.float32, device=dev)
+    dk = [torch.zeros((wl.batch, wl.kv_len, wl.heads, wl.head_dim), dtype=torch.float32, device=dev) for _ in kb]
+    dv = [torch.zeros_like(t) for t in dk]
+
+    def step():
+        ra.ringattn_ring_bwd(desc, x.q, kb, vb, pos, o, do, lse, delta, dq, dk, dv)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # one clean pass for the checks
+    for t in dk + dv:
+        t.zero_()
+    step()
+    torch.cuda.synchronize()
+    f = bwd_flops(wl)
+    # three windows of consecutive rows (first, seeded, last): the oracle's
+    # cost is in the keys, so a window costs what one row does
+    r0 = int(np.random.default_rng(2).integers(4, wl.q_len - 12))
+    windows = [(0, 4), (r0, r0 + 8), (wl.q_len - 4, wl.q_len)]
+    rows = [r for a, b in windows for r in range(a, b)]
+    rows_np = np.asarray(rows)
+    q_host, k_host, v_host, do_host = x.q.cpu(), x.k.cpu(), x.v.cpu(), do.cpu()
+    dq_host = dq.cpu().double().numpy()
+    fro_num = fro_den = 0.0
+    inv_err = 0.0
+    porder = list(range(wl.num_blocks))
+    for h in sample_heads:
+        qh = q_host[:, rows_np, h:h + 1, :].float().double().numpy()
+        doh = do_host[:, rows_np, h:h + 1, :].float().double().numpy()
+        kbh = [k_host[:, j * wl.kv_len:(j + 1) * wl.kv_len, h:h + 1, :].float().double().numpy() for j in porder]
+        vbh = [v_host[:, j * wl.kv_len:(j + 1) * wl.kv_len, h:h + 1, :].float().double().numpy() for j in porder]
+        i = 0
+        for a, b in windows:  # dQ rows are independent: each window at its own positions
+            rq, _, _ = oracle.ring_attention_bwd(qh[:, i:i + b - a], kbh, vbh, wl.q_pos0 + a,
+                                                 [wl.kv_pos0(j) for j in porder], wl.causal, doh[:, i:i + b - a])
+            g = dq_host[:, a:b, h:h + 1, :]
+            fro_num += float(((g - rq) ** 2).sum())
+            fro_den += float((rq ** 2).sum())
+            i += b - a
+        sdk = sum(t[:, :, h].double().sum(dim=1) for t in dk).cpu().numpy()
+        sdv = sum(t[:, :, h].double().sum(dim=1) for t in dv).cpu().numpy()
+        sdo = do_host[:, :, h].double().sum(dim=1).numpy()
+        mag = sum(t[:, :, h].double().abs().sum(dim=1) for t in dv).cpu().numpy()
+        inv_err = max(inv_err, float(np.abs(sdv - sdo).max() / mag.max()),
+                      float(np.abs(sdk).max() / sum(t[:, :, h].double().abs().sum(dim=1) for t in dk).max().item()))
+    fro = (fro_num / fro_den) ** 0.5 if fro_den else 0.0
+    ok = fro <= 5e-3 and inv_err <= 1e-3
+    return {
+        "ms_per_step": ms, "steps": steps, "warmup": warmup, "value": f / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "pct_of_bf16_peak": 100.0 * f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic_flop_per_step": f,
+        "kernels": "bwd_dq_kernel + bwd_dkdv_kernel per block, bwd_delta_kernel, fill_zero_kernel",
+        "parity_sampled": {"dq_rows": len(rows) * len(sample_heads), "dq_rel_fro": fro,
+                           "sum_dk_dv_invariants_rel": inv_err, "pass": bool(ok)},
+    }
 
 
 def cpu_baseline(x, wl, o, lse, heads=None, extra_rows=94):
@@ -154,6 +244,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--perblock", action="store_true", help="per-block path instead of the fused kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--bwd-steps", type=int, default=3)
     ap.add_argument("--traffic-calib", action="store_true",
                     help="also run one 1 GiB plain copy kernel (byte-counter calibration)")
     args = ap.parse_args()
@@ -302,6 +394,9 @@ def main():
         result["parity_sampled"] = parity
     else:
         result["cpu_baseline"] = None
+    if not args.no_backward and wl.dtype == "bf16" and not wl.host_streamed:
+        heads = [0, wl.heads - 1]
+        result["backward"] = backward_measure(x, wl, kb, vb, pos, o, lse, args.bwd_steps, 1, heads)
     print(json.dumps(result), flush=True)
 
 

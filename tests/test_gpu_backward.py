@@ -221,3 +221,37 @@ def test_medium_backward_matches_oracle():
         out.append(_check(dk[i], rk[i], f"dK block {j}"))
         out.append(_check(dv[i], rv[i], f"dV block {j}"))
     print(out)
+
+
+def test_full_size_backward_sampled():
+    """32768 query rows against 8 blocks of 32768 keys, 16 heads, causal, last
+    device of the ring, in the launch configuration the benchmark times: dQ of
+    two windows of rows of two heads against the oracle; for every head,
+    sum_c dK_c = 0 (a common shift of all keys leaves every softmax row
+    unchanged) and sum_c dV_c = sum_r dO_r (every row sees a key and its
+    softmax row sums to 1), in fp64 over the fp32 results."""
+    wl = inputs.CONFIGS[2]
+    print(f"config 2: {wl.name}", flush=True)
+    x = inputs.make_inputs(wl, cuda(), seed=0)
+    do = inputs.make_grad(wl, cuda(), seed=1)
+    order = ra.ringattn_ring_order(wl.q_idx, wl.num_blocks)
+    kv_pos0s = [wl.kv_pos0(j) for j in range(wl.num_blocks)]
+    dq, dk, dv = _run(x, do, order, kv_pos0s, wl.q_pos0, True)
+    assert torch.isfinite(dq).all() and all(torch.isfinite(t).all() for t in dk + dv)
+    for h in (0, wl.heads - 1):
+        kbh = [inputs.to_f64(x.k_block(j)[:, :, h:h + 1, :]) for j in range(wl.num_blocks)]
+        vbh = [inputs.to_f64(x.v_block(j)[:, :, h:h + 1, :]) for j in range(wl.num_blocks)]
+        for a, b in ((0, 4), (wl.q_len - 8, wl.q_len)):
+            q = inputs.to_f64(x.q[:, a:b, h:h + 1, :])
+            g = inputs.to_f64(do[:, a:b, h:h + 1, :])
+            rq, _, _ = oracle.ring_attention_bwd(q, kbh, vbh, wl.q_pos0 + a, kv_pos0s, True, g)
+            print(_check(dq[:, a:b, h:h + 1, :], rq, f"dQ rows {a}..{b - 1} head {h}"))
+    for h in range(wl.heads):
+        sdk = sum(t[:, :, h].double().sum(dim=1) for t in dk)
+        mk = sum(t[:, :, h].double().abs().sum(dim=1) for t in dk).max()
+        sdv = sum(t[:, :, h].double().sum(dim=1) for t in dv)
+        mv = sum(t[:, :, h].double().abs().sum(dim=1) for t in dv).max()
+        sdo = do[:, :, h].double().sum(dim=1)
+        ek = float(sdk.abs().max() / mk)
+        ev = float((sdv - sdo).abs().max() / mv)
+        assert ek <= 1e-3 and ev <= 1e-3, (h, ek, ev)
