@@ -11,13 +11,20 @@
 // block it receives, its contribution to that block's dK and dV, which in the
 // ring travel on with the block.  All three are accumulated (+=) in fp32.
 //
-// Two kernels per block:
-//   dq kernel:   a workgroup owns query rows and streams the block's key tiles
-//                (the forward's structure): S^T = K Q^T, dP^T = V dO^T, then
+// Two kernels per block, eight waves per workgroup (two per SIMD, so one
+// wave's MFMAs overlap the other's exponentials, LDS reads and barrier), each
+// streaming tiles through a three-stage LDS ring of direct global->LDS copies
+// (the copy of tile t+2 is in flight while tile t is computed):
+//   dq kernel:   a workgroup owns 256 query rows (32 per wave) and streams
+//                the block's 64-key tiles: S^T = K Q^T, dP^T = V dO^T, then
 //                dQ^T += K^T dS^T.  Q and dO fragments stay in registers.
-//   dkdv kernel: a workgroup owns keys (K, V fragments in registers) and
-//                streams query tiles: S = Q K^T, dP = dO V^T, then
-//                dV^T += dO^T P and dK^T += Q^T dS.
+//   dkdv kernel: a workgroup owns 256 keys (32 per wave; K (and V)
+//                fragments in registers) and streams 32-row query tiles, with
+//                the tile's LSE (and delta) copied into LDS beside Q and dO,
+//                in two passes that each fit two waves per SIMD: S = Q K^T,
+//                P, dV^T += dO^T P; then S, dP = dO V^T, dS, dK^T += Q^T dS.
+//                The second S costs 2 D flops per visible pair on top of the
+//                12 D of the five products plus the dq kernel's S and dP.
 // Matrix products use v_mfma_f32_32x32x16_bf16 with the same operand layouts
 // as the forward kernel: transposed-operand fragments (K^T, dO^T, Q^T) come
 // from LDS with ds_read_b64_tr_b16 in the 4-row-group key order that matches
@@ -28,41 +35,51 @@
 namespace ra {
 namespace {
 
-constexpr int kBWaves = 4;                 // waves per workgroup in both kernels
+constexpr int kBWaves = 8;                 // waves per workgroup in both kernels
 constexpr int kBThreads = 64 * kBWaves;
 constexpr int BQ = 32 * kBWaves;           // dq kernel: query rows per workgroup
 constexpr int BKN = 64;                    // dq kernel: keys per tile
 constexpr int BKK = 32 * kBWaves;          // dkdv kernel: keys per workgroup
 constexpr int BQT = 32;                    // dkdv kernel: query rows per tile
+constexpr int kStages = 3;                 // LDS ring depth
 
 template <int D>
 struct BCfg {
-  static constexpr int CH = D / 8;
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int ROWB = D * 2;
-  static constexpr int KT = BKN * ROWB;  // bytes of a 64-key tile
-  static constexpr int QT = BQT * ROWB;  // bytes of a 32-row tile
-  static constexpr int DQ_LDS = 2 * 3 * KT;   // two buffers of (K rows, K transposed reads, V rows)
-  static constexpr int DKDV_LDS = 2 * 4 * QT;  // two buffers of (Q, Q transposed, dO, dO transposed)
+  static constexpr int KT = BKN * ROWB;        // bytes of a 64-key tile
+  static constexpr int QT = BQT * ROWB;        // bytes of a 32-row tile
+  // dq stage: K rows (row-read placement), K (transpose-read placement), V rows
+  static constexpr int DQ_STAGE = 3 * KT;
+  static constexpr int DQ_LDS = kStages * DQ_STAGE;
+  static constexpr int DQ_CPW = DQ_STAGE / 1024 / kBWaves;  // 1 KiB copies per wave per tile
+  static_assert(DQ_STAGE % (1024 * kBWaves) == 0, "copies per wave");
+  static_assert(DQ_LDS <= 160 * 1024, "LDS budget");
 };
 
-// Copy rows 0..nrows-1 of a row-major bf16 tile (row r at src + r*row_bytes)
-// into LDS at dst, chunk placement swizzled for row reads (VSWZ false, as
-// k_off) or for transpose reads (VSWZ true, as v_off).  Rows at or past
-// `valid` re-read row valid-1 (their values are masked out).  The copies of
-// the workgroup are shared out over its waves; wait with vmcnt before use.
-template <int D, bool VSWZ>
-__device__ __forceinline__ void copy_tile(const char* src, int64_t row_bytes, int valid, uint32_t dst, int nrows,
-                                          int wave, int lane) {
-  const int nchunks = nrows * D * 2 / 1024;
-  for (int c = wave; c < nchunks; c += kBWaves) {
+// Issue this wave's share of the copies of one stage: NCOPY row-major tiles of
+// `nrows` rows each (tile j from srcs[j], rows at row_bytes apart), placed
+// back to back at dst with the row-read placement (k_off) or, where bit j of
+// tr_mask is set, the transpose-read placement (v_off).  Rows at or past
+// `valid` re-read row valid-1 (their values are masked out later).  Every
+// wave issues exactly CPW copies, so one vmcnt bound covers every wave.
+template <int D, int NCOPY, int CPW>
+__device__ __forceinline__ void copy_stage(const char* const (&srcs)[NCOPY], int tr_mask, int64_t row_bytes,
+                                           int valid, uint32_t dst, int nrows, int wave, int lane) {
+  const int per_copy = nrows * D * 2 / 1024;
+#pragma unroll
+  for (int j = 0; j < CPW; ++j) {
+    const int g = wave + kBWaves * j;
+    const int cp = g / per_copy;
+    const int c = g - cp * per_copy;
     const int p = c * 1024 + lane * 16;
     const int row = p / (D * 2);
     const int cs = (p % (D * 2)) / 16;
-    const int col = (VSWZ ? v_off<D>(row, cs) : k_off<D>(row, cs)) / 16 - row * (D / 8);  // XOR is self-inverse
+    const bool tr = (tr_mask >> cp) & 1;
+    const int col = (tr ? v_off<D>(row, cs) : k_off<D>(row, cs)) / 16 - row * (D / 8);  // XOR is self-inverse
     const int rr = row < valid ? row : valid - 1;
-    lds_dma16(src, (uint32_t)(rr * row_bytes + col * 16), dst + c * 1024);
+    lds_dma16(srcs[cp], (uint32_t)(rr * row_bytes + col * 16), dst + cp * (nrows * D * 2) + c * 1024);
   }
 }
 
@@ -91,10 +108,24 @@ __device__ __forceinline__ int tr_base(int lane) {
 // Row of element i of a 32x32 MFMA result held by a lane in half hf.
 __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + (i & 3) + 4 * hf; }
 
+__device__ __forceinline__ bf16x8 pack8(const bf16x2 (&x)[16], int q0) {
+  const bf16x4 lo = __builtin_shufflevector(x[q0], x[q0 + 1], 0, 1, 2, 3);
+  const bf16x4 hi = __builtin_shufflevector(x[q0 + 2], x[q0 + 3], 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ bf16x8 pack8(const bf16x2 (&x)[8], int q0) {
+  const bf16x4 lo = __builtin_shufflevector(x[q0], x[q0 + 1], 0, 1, 2, 3);
+  const bf16x4 hi = __builtin_shufflevector(x[q0 + 2], x[q0 + 3], 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Clamp a 64-bit tile-relative bound into [lo, hi] as int.
+__device__ __forceinline__ int clamp_i(int64_t x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : (int)x); }
+
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per BQ query rows of one (b, h); this lane's row r.
 template <int D>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
   using C = BCfg<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int n_qt = (int)((a.q_len + BQ - 1) / BQ);
@@ -141,11 +172,19 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   }
   const int64_t sidx = ((int64_t)b * a.heads + h) * a.q_len + (row_ok ? r : 0);
   const float lse_r = a.lse[sidx];
+  const float dlt_r = a.delta[sidx];
+  wait_vm<0>();  // the register loads above, before any copy is in flight
   const bool row_live = row_ok && lse_r > -INFINITY;  // a row that saw no key anywhere has no gradient
   const float lse2 = row_live ? lse_r * kLog2e : 0.f;
-  const float dlt = row_live ? a.delta[sidx] : 0.f;
+  const float dlt = row_live ? dlt_r : 0.f;
   const float c2 = a.scale * kLog2e;
-  const int64_t my_pos = a.q_pos0 + r;
+  // keys visible to this row: [0, klim) of the block
+  int64_t klim = a.kv_len;
+  if (a.causal) {
+    const int64_t e = a.q_pos0 + r - a.kv_pos0 + 1;
+    klim = e < klim ? e : klim;
+  }
+  if (!row_live) klim = 0;
 
   f32x16 acc[C::DB];
 #pragma unroll
@@ -155,68 +194,69 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   const int64_t row_bytes = a.kv_ss * 2;
   const char* ksrc = (const char*)a.k + (b * a.kv_sb + h * a.kv_sh) * 2;
   const char* vsrc = (const char*)a.v + (b * a.kv_sb + h * a.kv_sh) * 2;
-  auto issue = [&](int t, int buf) {
+  auto issue = [&](int t) {
     const int64_t go = (int64_t)t * BKN * row_bytes;
-    const int valid = (int)(a.kv_len - (int64_t)t * BKN);
-    const uint32_t dst = base + buf * 3 * C::KT;
-    copy_tile<D, false>(ksrc + go, row_bytes, valid, dst, BKN, wave, lane);
-    copy_tile<D, true>(ksrc + go, row_bytes, valid, dst + C::KT, BKN, wave, lane);
-    copy_tile<D, false>(vsrc + go, row_bytes, valid, dst + 2 * C::KT, BKN, wave, lane);
+    const char* const srcs[3] = {ksrc + go, ksrc + go, vsrc + go};
+    copy_stage<D, 3, C::DQ_CPW>(srcs, 0b010, row_bytes, (int)(a.kv_len - (int64_t)t * BKN),
+                               base + (t % kStages) * C::DQ_STAGE, BKN, wave, lane);
   };
   const int vA = tr_base<D>(lane);
 
-  issue(0, 0);
-  wait_vm<0>();
+  issue(0);
+  if (n_tiles > 1) {
+    issue(1);
+    wait_vm<C::DQ_CPW>();
+  } else {
+    wait_vm<0>();
+  }
   wg_barrier();
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) issue(t + 1, (t + 1) & 1);
-    const uint32_t kl = base + (t & 1) * 3 * C::KT;
+    if (t + 2 < n_tiles) issue(t + 2);
+    const uint32_t kl = base + (t % kStages) * C::DQ_STAGE;
     const uint32_t ktl = kl + C::KT;
     const uint32_t vl = kl + 2 * C::KT;
-    // S^T = K Q^T and dP^T = V dO^T (rows: 64 keys in two 32-key halves kb)
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int o = k_off<D>(l32 + 32 * kb, 2 * ks + hf);
-        const bf16x8 kf = *(lds_bf16x8*)(size_t)(kl + o);
-        const bf16x8 vf = *(lds_bf16x8*)(size_t)(vl + o);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, df[ks], ks == 0 ? f32x16{} : dp[kb], 0, 0, 0);
-      }
-    // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - LSE2); packed to bf16 pairs
+    const int kv_rel = clamp_i(klim - (int64_t)t * BKN, 0, BKN);  // visible keys of this tile: [0, kv_rel)
     bf16x2 dsp[16];
-    const int64_t key_t0 = (int64_t)t * BKN;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      float v2[2];
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T = K Q^T and dP^T = V dO^T for keys 32 kb .. 32 kb + 31 of the tile
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 2 * q + u;
-        const int kb = e >> 4, i = e & 15;
-        const int64_t key = key_t0 + 32 * kb + acc_row(i, hf);
-        const bool vis = row_live && key < a.kv_len && (!a.causal || a.kv_pos0 + key <= my_pos);
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, -lse2)) : 0.f;
-        v2[u] = p * (dp[kb][i] - dlt);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const int o = k_off<D>(l32 + 32 * kb, 2 * ks + hf);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(kl + o), qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(vl + o), df[ks], dp, 0, 0, 0);
       }
-      dsp[q] = bf16x2{(__bf16)v2[0], (__bf16)v2[1]};
+      // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - LSE2), bf16 pairs
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float v2[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = 2 * q + u;
+          const bool vis = 32 * kb + acc_row(i, hf) < kv_rel;
+          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2)) : 0.f;
+          v2[u] = p * (dp[i] - dlt);
+        }
+        dsp[8 * kb + q] = bf16x2{(__bf16)v2[0], (__bf16)v2[1]};
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep each half's operands short-lived (register budget)
     }
     // dQ^T += K^T dS^T
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        const int q0 = 8 * kb + 4 * tp;
-        const bf16x4 lo = __builtin_shufflevector(dsp[q0], dsp[q0 + 1], 0, 1, 2, 3);
-        const bf16x4 hi = __builtin_shufflevector(dsp[q0 + 2], dsp[q0 + 3], 0, 1, 2, 3);
-        const bf16x8 pf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 pf = pack8(dsp, 8 * kb + 4 * tp);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ktl, vA, db, 32 * kb + 16 * tp), pf, acc[db],
                                                             0, 0, 0);
       }
-    wait_vm<0>();
+    if (t + 2 < n_tiles)
+      wait_vm<C::DQ_CPW>();  // tile t+1 landed; t+2 may still be in flight
+    else
+      wait_vm<0>();
     wg_barrier();
   }
   if (!row_ok) return;
@@ -234,10 +274,28 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per BKK keys of one (b, h); this lane's key c (as the
-// column of the 32x32 products).
-template <int D>
-__global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+// column of the 32x32 products).  Two passes over the query tiles keep each
+// within two waves' register budget: PASS 0 forms S = Q K^T and P and
+// accumulates dV^T += dO^T P; PASS 1 forms S and dP = dO V^T, dS = P (dP -
+// delta) and accumulates dK^T += Q^T dS.
+template <int D, int PASS>
+struct KvStage {
+  static constexpr int QT = BQT * D * 2;
+  static constexpr int NCOPY = PASS == 0 ? 2 : 3;   // PASS 0: Q rows, dO^T; PASS 1: Q rows, dO rows, Q^T
+  static constexpr int TR_MASK = PASS == 0 ? 0b10 : 0b100;
+  static constexpr int LSE_OFF = NCOPY * QT;
+  static constexpr int DLT_OFF = NCOPY * QT + 256;
+  static constexpr int BYTES = NCOPY * QT + (PASS == 0 ? 256 : 512);
+  static constexpr int LDS = kStages * BYTES;
+  static constexpr int TOTAL = NCOPY * QT / 1024;                 // 1 KiB copies per tile
+  static constexpr int CPW = (TOTAL + kBWaves - 1) / kBWaves;     // per wave (the last round may repeat a copy)
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int D, int PASS>
+__global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<D>;
+  using S = KvStage<D, PASS>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int n_kt = (int)((a.kv_len + BKK - 1) / BKK);
   const int n_work = a.batch * a.heads * n_kt;
@@ -266,116 +324,138 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_qt = (int)((a.q_len + BQT - 1) / BQT);
   const int qt0 = (int)(r_min / BQT);
 
-  bf16x8 kfr[C::KS], vfr[C::KS];
+  bf16x8 kfr[C::KS], vfr[PASS == 1 ? C::KS : 1];
   {
     const int64_t off = b * a.kv_sb + c * a.kv_ss + h * a.kv_sh + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (key_ok) {
         kfr[ks] = *(const bf16x8*)((const __bf16*)a.k + off + 16 * ks);
-        vfr[ks] = *(const bf16x8*)((const __bf16*)a.v + off + 16 * ks);
+        if constexpr (PASS == 1) vfr[ks] = *(const bf16x8*)((const __bf16*)a.v + off + 16 * ks);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kfr[ks][j] = vfr[ks][j] = (__bf16)0.0f;
+        for (int j = 0; j < 8; ++j) {
+          kfr[ks][j] = (__bf16)0.0f;
+          if constexpr (PASS == 1) vfr[ks][j] = (__bf16)0.0f;
+        }
       }
     }
   }
+  wait_vm<0>();  // the register loads above, before any copy is in flight
   const float c2 = a.scale * kLog2e;
-  const int64_t key_pos = a.kv_pos0 + c;
-  f32x16 dk[C::DB], dv[C::DB];
+  const int64_t first_row = a.causal ? a.kv_pos0 + c - a.q_pos0 : 0;  // first row (chunk-relative) seeing key c
+  f32x16 acc[C::DB];
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) dk[db] = dv[db] = f32x16{};
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
   const uint32_t base = lds_addr_of(lds);
   const int64_t qrow_bytes = a.q_ss * 2;
   const char* qsrc = (const char*)a.q + (b * a.q_sb + h * a.q_sh) * 2;
   const char* osrc = (const char*)a.dout + (b * a.q_sb + h * a.q_sh) * 2;
-  const float* lse_bh = a.lse + ((int64_t)b * a.heads + h) * a.q_len;
-  const float* dl_bh = a.delta + ((int64_t)b * a.heads + h) * a.q_len;
-  auto issue = [&](int t, int buf) {
+  const char* lse_bh = (const char*)(a.lse + ((int64_t)b * a.heads + h) * a.q_len);
+  const char* dl_bh = (const char*)(a.delta + ((int64_t)b * a.heads + h) * a.q_len);
+  auto issue = [&](int t) {
+    const uint32_t st = base + (t % kStages) * S::BYTES;
+    const int64_t row = (int64_t)t * BQT + l32;
+    const uint32_t roff = (uint32_t)((row < a.q_len ? row : a.q_len - 1) * 4);
+    // waves 0 and 1 also copy the tile's LSE and delta (before the tiles, so
+    // the common vmcnt bound below covers them too)
+    if (wave == 0) lds_dma4(lse_bh, roff, st + S::LSE_OFF);
+    if (PASS == 1 && wave == 1) lds_dma4(dl_bh, roff, st + S::DLT_OFF);
     const int64_t go = (int64_t)t * BQT * qrow_bytes;
     const int valid = (int)(a.q_len - (int64_t)t * BQT);
-    const uint32_t dst = base + buf * 4 * C::QT;
-    copy_tile<D, false>(qsrc + go, qrow_bytes, valid, dst, BQT, wave, lane);
-    copy_tile<D, true>(qsrc + go, qrow_bytes, valid, dst + C::QT, BQT, wave, lane);
-    copy_tile<D, false>(osrc + go, qrow_bytes, valid, dst + 2 * C::QT, BQT, wave, lane);
-    copy_tile<D, true>(osrc + go, qrow_bytes, valid, dst + 3 * C::QT, BQT, wave, lane);
+    const int per_copy = S::QT / 1024;
+#pragma unroll
+    for (int j = 0; j < S::CPW; ++j) {
+      int g = wave + kBWaves * j;
+      if (g >= S::TOTAL) g -= S::TOTAL;  // repeat a copy another wave makes (same bytes, same place)
+      const int cp = g / per_copy;
+      const int cc = g - cp * per_copy;
+      const int p = cc * 1024 + lane * 16;
+      const int rw = p / (D * 2);
+      const int cs = (p % (D * 2)) / 16;
+      const bool tr = (S::TR_MASK >> cp) & 1;
+      const int col = (tr ? v_off<D>(rw, cs) : k_off<D>(rw, cs)) / 16 - rw * (D / 8);  // XOR is self-inverse
+      const int rr = rw < valid ? rw : valid - 1;
+      const char* src = cp == 1 ? osrc + go : qsrc + go;  // copy 1 is dO in both passes
+      lds_dma16(src, (uint32_t)(rr * qrow_bytes + col * 16), st + cp * S::QT + cc * 1024);
+    }
   };
   const int vA = tr_base<D>(lane);
 
-  issue(qt0, qt0 & 1);
-  wait_vm<0>();
+  issue(qt0);
+  if (qt0 + 1 < n_qt) {
+    issue(qt0 + 1);
+    wait_vm<S::CPW>();
+  } else {
+    wait_vm<0>();
+  }
   wg_barrier();
   for (int t = qt0; t < n_qt; ++t) {
-    if (t + 1 < n_qt) issue(t + 1, (t + 1) & 1);
-    const uint32_t ql = base + (t & 1) * 4 * C::QT;
-    const uint32_t qtl = ql + C::QT;
-    const uint32_t ol = ql + 2 * C::QT;
-    const uint32_t otl = ql + 3 * C::QT;
-    // S = Q K^T and dP = dO V^T (rows: the tile's 32 queries; columns: keys)
-    f32x16 s = f32x16{}, dp = f32x16{};
+    if (t + 2 < n_qt) issue(t + 2);
+    const uint32_t st = base + (t % kStages) * S::BYTES;
+    const uint32_t ql = st;                                       // Q rows
+    const uint32_t trl = st + (PASS == 0 ? 1 : 2) * S::QT;        // dO^T (PASS 0) or Q^T (PASS 1)
+    // S = Q K^T (and dP = dO V^T): rows the tile's 32 queries, columns keys
+    f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       const int o = k_off<D>(l32, 2 * ks + hf);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(ql + o), kfr[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(ol + o), vfr[ks], dp, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(ql + o), kfr[ks], sc, 0, 0, 0);
+      if constexpr (PASS == 1)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(st + S::QT + o), vfr[ks], dp, 0, 0, 0);
     }
-    // P = exp2(S c - LSE2[row]), dS = P (dP - delta[row]); bf16 pairs of
-    // consecutive elements (rows 8 (i>>2) + (i&3) + 4 hf)
-    bf16x2 pp[8], dsp[8];
+    // rows of this tile that see key c: [lo, hi)
     const int64_t row_t0 = (int64_t)t * BQT;
+    const int lo = key_ok ? clamp_i(first_row - row_t0, 0, BQT) : BQT;
+    const int hi = clamp_i(a.q_len - row_t0, 0, BQT);
+    // P = exp2(S c - LSE2[row]) (PASS 0) or dS = P (dP - delta[row]) (PASS 1),
+    // as bf16 pairs of consecutive elements (rows 8 (i>>2) + (i&3) + 4 hf)
+    bf16x2 x[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      float pv[2], dv2[2];
+    for (int g = 0; g < 4; ++g) {
+      typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+      const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (8 * g + 4 * hf) * 4);
+      f32x4 d4 = f32x4{};
+      if constexpr (PASS == 1) d4 = *(lds_f32x4*)(size_t)(st + S::DLT_OFF + (8 * g + 4 * hf) * 4);
+      float v[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = 2 * q + u;
-        const int64_t row = row_t0 + acc_row(i, hf);
-        const int64_t rc = row < a.q_len ? row : a.q_len - 1;
-        const float lse_r = lse_bh[rc];
-        const bool vis = key_ok && row < a.q_len && lse_r > -INFINITY &&
-                         (!a.causal || key_pos <= a.q_pos0 + row);
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse_r * kLog2e)) : 0.f;
-        pv[u] = p;
-        dv2[u] = p * (dp[i] - (vis ? dl_bh[rc] : 0.f));
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * g + j;
+        const int row = acc_row(i, hf);
+        const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, -l4[j] * kLog2e)) : 0.f;
+        v[j] = PASS == 0 ? p : p * (dp[i] - (vis ? d4[j] : 0.f));
       }
-      pp[q] = bf16x2{(__bf16)pv[0], (__bf16)pv[1]};
-      dsp[q] = bf16x2{(__bf16)dv2[0], (__bf16)dv2[1]};
+      x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+      x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
     }
-    // dV^T += dO^T P and dK^T += Q^T dS (contraction over the 32 rows in two
+    // dV^T += dO^T P or dK^T += Q^T dS (contraction over the 32 rows in two
     // 16-row steps tp)
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) {
-      const bf16x4 plo = __builtin_shufflevector(pp[4 * tp], pp[4 * tp + 1], 0, 1, 2, 3);
-      const bf16x4 phi = __builtin_shufflevector(pp[4 * tp + 2], pp[4 * tp + 3], 0, 1, 2, 3);
-      const bf16x8 pf = __builtin_shufflevector(plo, phi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x4 slo = __builtin_shufflevector(dsp[4 * tp], dsp[4 * tp + 1], 0, 1, 2, 3);
-      const bf16x4 shi = __builtin_shufflevector(dsp[4 * tp + 2], dsp[4 * tp + 3], 0, 1, 2, 3);
-      const bf16x8 sf = __builtin_shufflevector(slo, shi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 xf = pack8(x, 4 * tp);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(otl, vA, db, 16 * tp), pf, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qtl, vA, db, 16 * tp), sf, dk[db], 0, 0, 0);
-      }
+      for (int db = 0; db < C::DB; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(trl, vA, db, 16 * tp), xf, acc[db], 0, 0, 0);
     }
-    wait_vm<0>();
+    if (t + 2 < n_qt)
+      wait_vm<S::CPW>();  // tile t+1 (and its LSE, delta) landed
+    else
+      wait_vm<0>();
     wg_barrier();
   }
   if (!key_ok) return;
-  const int64_t o = (((int64_t)b * a.kv_cap + c) * a.heads + h) * D + 4 * hf;
+  float* out = (PASS == 0 ? a.dv : a.dk) + (((int64_t)b * a.kv_cap + c) * a.heads + h) * D + 4 * hf;
+  const float f = PASS == 0 ? 1.f : a.scale;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      f32x4 k4 = *(f32x4*)(a.dk + o + 32 * db + 8 * g);
-      f32x4 v4 = *(f32x4*)(a.dv + o + 32 * db + 8 * g);
+      f32x4 v4 = *(f32x4*)(out + 32 * db + 8 * g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        k4[j] += a.scale * dk[db][4 * g + j];
-        v4[j] += dv[db][4 * g + j];
-      }
-      *(f32x4*)(a.dk + o + 32 * db + 8 * g) = k4;
-      *(f32x4*)(a.dv + o + 32 * db + 8 * g) = v4;
+      for (int j = 0; j < 4; ++j) v4[j] += f * acc[db][4 * g + j];
+      *(f32x4*)(out + 32 * db + 8 * g) = v4;
     }
 }
 
@@ -387,8 +467,11 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
     hipError_t e =
         hipFuncSetAttribute((const void*)bwd_dq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, C::DQ_LDS);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            C::DKDV_LDS);
+    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            KvStage<D, 0>::LDS);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            KvStage<D, 1>::LDS);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
@@ -399,9 +482,13 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (nk > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(((nk + 7) / 8) * 8)), dim3(kBThreads), C::DKDV_LDS, s,
-                       a);
+  if (nk > 0) {
+    const dim3 grid((unsigned)(((nk + 7) / 8) * 8));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 0>), grid, dim3(kBThreads), (KvStage<D, 0>::LDS), s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), grid, dim3(kBThreads), (KvStage<D, 1>::LDS), s, a);
+  }
   return hipGetLastError();
 }
 

@@ -70,6 +70,25 @@ __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint3
       : "memory");
 }
 
+// The same for 4 bytes per lane (global_load_lds_dword): lane i's dword lands
+// at LDS byte lds_addr + 4 i.
+__device__ __forceinline__ void lds_dma4(const char* base, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t bv = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
 // LDS byte address of a generic pointer into the dynamic LDS array.
 __device__ __forceinline__ uint32_t lds_addr_of(const char* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
