@@ -29,6 +29,10 @@ What it computes, and from which passage:
   that output with respect to Q, K and V for an upstream dO (the pages train
   through the ring but never write the backward pass; the reading is stated
   in that module).
+* ``blockwise_ffn`` / ``gelu_tanh`` (``ffn.py``): the position-wise
+  feedforward computed over row blocks ("Ring Attention with Blockwise
+  Transformers for Near-Infinite Context", Abstract: blockwise computation of
+  self-attention and feedforward); its readings are stated in that module.
 
 Every function is pinned by tests in ``tests/test_oracle_pins.py`` against
 brute force in 50-digit arithmetic, closed forms, invariants and a library
@@ -43,3 +47,4 @@ from .attention import (  # noqa: F401
     visible,
 )
 from .backward import delta, ring_attention_bwd  # noqa: F401
+from .ffn import blockwise_ffn, gelu_tanh  # noqa: F401
