@@ -14,6 +14,11 @@ and LSE, in algorithmic TFLOP/s (10*B*H*D*(visible pairs): the five products
 S, dP, dQ, dK, dV), with dQ checked against the oracle on sampled rows and the
 sums of dK and dV over all keys checked against their closed forms.
 
+Unless --no-ffn, it also carries `ffn`: the blockwise feedforward of the
+1.3B model's layer (d 2048, d_ff 8192, tanh GELU) over the same 128K-row
+chunk in 16K-row blocks, in TFLOP/s of its two products (4*rows*d*d_ff),
+with sampled rows checked against the oracle.
+
 Prints ONE JSON line.  `value` is causal-adjusted TFLOP/s: 4*B*H*D*(visible
 query-key pairs) per step over the measured step time.  `roofline` prices the
 fused attention kernel's live-measured duration (HIP events on the launch
@@ -21,7 +26,7 @@ stream) against the bf16 dense MFMA peak.  `cpu_baseline` times the fp64 CPU
 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
-       [--perblock] [--no-cpu-baseline] [--traffic-calib] [--no-backward] [--bwd-steps K]
+       [--perblock] [--no-cpu-baseline] [--traffic-calib] [--no-backward] [--bwd-steps K] [--no-ffn]
 """
 
 from __future__ import annotations
@@ -176,6 +181,46 @@ def backward_measure(x, wl, kb, vb, pos, o, lse, steps, warmup, sample_heads):
     }
 
 
+def ffn_measure(dev, steps, warmup):
+    """Time the blockwise feedforward at its workload and check sampled rows
+    against the oracle (rows are independent)."""
+    import numpy as np
+    import torch
+    import oracle
+    from long_context_exact_blockwise_amd import inputs
+    from long_context_exact_blockwise_amd import ringattn as ra
+    wl = inputs.FFN_CONFIG
+    x, w1, b1, w2, b2 = inputs.make_ffn_inputs(wl.rows, wl.d_model, wl.d_ff, dev, seed=0)
+    y = torch.empty_like(x)
+    ws = torch.empty((wl.block_rows, wl.d_ff), dtype=torch.bfloat16, device=dev)
+    desc = ra.ffn_desc(x, w1, y, wl.block_rows)
+    for _ in range(warmup):
+        ra.ringattn_ffn_fwd(desc, x, w1, b1, w2, b2, y, ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        ra.ringattn_ffn_fwd(desc, x, w1, b1, w2, b2, y, ws)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    f = 4 * wl.rows * wl.d_model * wl.d_ff
+    rows = inputs.sample_rows(wl.rows, extra=14, seed=3)
+    idx = torch.as_tensor(rows, device=dev)
+    f64 = lambda t: t.float().double().cpu().numpy()  # noqa: E731
+    ref = oracle.blockwise_ffn(f64(x.index_select(0, idx)), f64(w1), f64(b1), f64(w2), f64(b2))
+    g = f64(y.index_select(0, idx))
+    fro = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
+    mx = float(np.max(np.abs(g - ref)) / np.max(np.abs(ref)))
+    return {
+        "workload": wl.name, "ms_per_step": ms, "steps": steps, "value": f / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
+        "pct_of_bf16_peak": 100.0 * f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic_flop_per_step": f,
+        "kernels": "gemm_bt_kernel<gelu> + gemm_bt_kernel<plain> per block",
+        "parity_sampled": {"rows": len(rows), "rel_fro": fro, "max_abs_over_max": mx,
+                           "pass": bool(fro <= 5e-3 and mx <= 2e-2)},
+    }
+
+
 def cpu_baseline(x, wl, o, lse, heads=None, extra_rows=94):
     """Time the fp64 oracle on sampled rows of every head; also check those
     rows against the GPU output at the bf16 tolerances."""
@@ -246,6 +291,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=3)
+    ap.add_argument("--no-ffn", action="store_true", help="skip the feedforward measurement")
     ap.add_argument("--traffic-calib", action="store_true",
                     help="also run one 1 GiB plain copy kernel (byte-counter calibration)")
     args = ap.parse_args()
@@ -397,6 +443,8 @@ def main():
     if not args.no_backward and wl.dtype == "bf16" and not wl.host_streamed:
         heads = [0, wl.heads - 1]
         result["backward"] = backward_measure(x, wl, kb, vb, pos, o, lse, args.bwd_steps, 1, heads)
+    if not args.no_ffn:
+        result["ffn"] = ffn_measure(dev, 10, 2)
     print(json.dumps(result), flush=True)
 
 

@@ -210,6 +210,39 @@ ra_status ringattn_ring_bwd(const ra_desc* desc, const void* q, const void* cons
                             int32_t num_blocks, const void* o, const void* dout, const float* lse, float* delta,
                             float* dq, float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream);
 
+/* ---- Blockwise feedforward ("Ring Attention with Blockwise Transformers for
+ * Near-Infinite Context", Abstract: blockwise computation of self-attention
+ * and feedforward).  The pages do not write the network out; the reading
+ * taken is the position-wise y = gelu(x W1^T + b1) W2^T + b2 with the tanh
+ * form of GELU (Hendrycks and Gimpel), as in GPT-style language models such
+ * as the 1.3B model (hidden dim 2048) of "Ring Attention: Train 1M Tokens on
+ * 8GB GPUs in 2026", section "Memory Breakdown: 512K Tokens on 4x RTX 3090".
+ *
+ * All tensors bf16, row-major: x [rows, d_model] (row stride x_stride), W1
+ * [d_ff, d_model] and W2 [d_model, d_ff] dense (rows are output features, as
+ * in a Linear layer), b1 [d_ff], b2 [d_model], y [rows, d_model] (row stride
+ * y_stride).  The rows are processed in blocks of block_rows: per block the
+ * hidden activation (fp32-accumulated, GELU applied, rounded to bf16) is
+ * written to `workspace`, [block_rows, d_ff] bf16 dense, caller-owned device
+ * memory, then multiplied by W2.  The result does not depend on block_rows
+ * (each row's arithmetic is the same in any block).  For a chunk in the
+ * attention layout [B, S, H, D] with B = 1, x is that tensor with d_model =
+ * H*D and x_stride = H*D. */
+typedef struct ra_ffn_desc {
+  int64_t rows;       /* tokens of the chunk, >= 0                             */
+  int32_t d_model;    /* d: a multiple of 64, <= 16384                         */
+  int32_t d_ff;       /* F: a multiple of 64, <= 65536                         */
+  int64_t x_stride;   /* elements between rows of x: >= d_model, multiple of 8 */
+  int64_t y_stride;   /* elements between rows of y: >= d_model, multiple of 8 */
+  int64_t block_rows; /* rows per block (>= 1); workspace holds block_rows*d_ff */
+} ra_ffn_desc;
+
+/* y = feedforward(x), block by block, enqueued on `stream`.  rows = 0 checks
+ * the descriptor and enqueues nothing.  Pointers are device memory, 16-byte
+ * aligned; y must not overlap x, the weights or the workspace. */
+ra_status ringattn_ffn_fwd(const ra_ffn_desc* desc, const void* x, const void* w1, const void* b1, const void* w2,
+                           const void* b2, void* y, void* workspace, hipStream_t stream);
+
 /* Measurement helper, not part of the attention path: a plain device-to-device
  * copy kernel of `bytes` (multiple of 16, 16-byte aligned pointers), used to
  * calibrate hardware byte counters and HBM bandwidth. */

@@ -1,0 +1,177 @@
+// Blockwise feedforward of one device's chunk, bf16, gfx950.
+//
+// "Ring Attention with Blockwise Transformers for Near-Infinite Context"
+// (Abstract) computes the feedforward blockwise, like the attention.  The
+// network is the position-wise y = gelu(x W1^T + b1) W2^T + b2 (tanh-form
+// GELU; W1 [F, d], W2 [d, F], rows are output features).  The chunk's rows
+// are processed in blocks; per block the hidden activation [rows, F] lives in
+// a caller workspace (bf16, as P is rounded before its product in the
+// attention), so memory holds one block's activation, not the chunk's.
+//
+// Both layers are the same kernel: C[M, N] = A[M, K] B[N, K]^T + bias[N]
+// (then GELU for the first layer), bf16 in, fp32 accumulation, bf16 out.  A
+// workgroup of eight waves owns a 256 x 256 tile of C; a wave owns 64 rows x
+// 128 columns as 2 x 4 products of v_mfma_f32_32x32x16_bf16, computed
+// transposed (C^T = B A^T) so that a lane holds one row of C and stores runs
+// of 4 consecutive columns.  K advances 64 at a time through two LDS stages
+// filled by direct global->LDS copies, the next stage's copy in flight while
+// the current one is multiplied.
+#include "attn_common.h"
+#include "ra_internal.h"
+
+namespace ra {
+namespace {
+
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int GBM = 256;                          // rows of C per workgroup
+constexpr int GBN = 256;                          // columns of C per workgroup
+constexpr int GBK = 64;                           // contraction per stage
+constexpr int G_TILE = 256 * GBK * 2;             // 32 KiB: one operand tile (256 rows x 128 B)
+constexpr int G_STAGE = 2 * G_TILE;               // weights tile, then token tile
+constexpr int G_LDS = 2 * G_STAGE;                // two stages: 128 KiB
+constexpr int G_CPW = G_STAGE / 1024 / kGWaves;   // 1 KiB copies per wave per stage
+
+// GELU, tanh form (Hendrycks and Gimpel): 0.5 x (1 + tanh(sqrt(2/pi) (x +
+// 0.044715 x^3))), with tanh(u) = 1 - 2 / (1 + e^(2u)) (exact at both
+// saturations: e^(2u) -> inf gives 1, -> 0 gives -1).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * x, x * x, x);
+  const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * u);
+  const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
+  return 0.5f * x * (1.f + t);
+}
+
+template <bool GELU>
+__global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tiles_n = (g.n + GBN - 1) / GBN;
+  const int64_t tiles_m = (g.m + GBM - 1) / GBM;
+  const int64_t n_work = tiles_m * tiles_n;
+  const int64_t per = (n_work + 7) >> 3;
+  // consecutive workgroups go to different XCDs; each XCD takes a contiguous
+  // run of tiles (row-major over (m tile, n tile)), so its L2 sees one token
+  // tile against a run of weight tiles
+  const int64_t wid = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (wid >= n_work) return;
+  const int64_t tm = wid / tiles_n;
+  const int tn = (int)(wid - tm * tiles_n);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int wn = wave & 1;   // 128-column half of the tile
+  const int wm = wave >> 1;  // 64-row quarter of the tile
+
+  const int64_t m0 = tm * GBM;
+  const int n0 = tn * GBN;
+  const char* wsrc = (const char*)(g.b + (int64_t)n0 * g.ldb);
+  const char* xsrc = (const char*)(g.a + m0 * g.lda);
+  const int64_t wrow = g.ldb * 2, xrow = g.lda * 2;
+  const int wvalid = g.n - n0 < GBN ? g.n - n0 : GBN;
+  const int xvalid = (int)(g.m - m0 < GBM ? g.m - m0 : GBM);
+  const uint32_t base = lds_addr_of(lds);
+  const int nk = g.k / GBK;
+
+  // this wave's share of a stage: 64 copies of 1 KiB (8 rows x 128 B), the
+  // first 32 of the weight tile, the rest of the token tile; rows past the
+  // matrix edge re-read its last row (their products are never stored)
+  auto issue = [&](int kt) {
+    const uint32_t st = base + (kt & 1) * G_STAGE;
+#pragma unroll
+    for (int j = 0; j < G_CPW; ++j) {
+      const int gi = wave + kGWaves * j;
+      const int cp = gi >> 5;
+      const int c = gi & 31;
+      const int p = c * 1024 + lane * 16;
+      const int row = p >> 7;
+      const int cs = (p & 127) >> 4;
+      const int col = k_off<64>(row, cs) / 16 - row * 8;  // XOR is self-inverse
+      const int valid = cp ? xvalid : wvalid;
+      const int rr = row < valid ? row : valid - 1;
+      const char* src = (cp ? xsrc : wsrc) + kt * (GBK * 2);
+      lds_dma16(src, (uint32_t)(rr * (cp ? xrow : wrow) + col * 16), st + cp * G_TILE + c * 1024);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) acc[ni][mi] = f32x16{};
+
+  issue(0);
+  wait_vm<0>();
+  wg_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) issue(kt + 1);
+    const uint32_t wl = base + (kt & 1) * G_STAGE;
+    const uint32_t xl = wl + G_TILE;
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+        af[ni] = *(lds_bf16x8*)(size_t)(wl + k_off<64>(wn * 128 + ni * 32 + l32, 2 * ks + hf));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+        bfr[mi] = *(lds_bf16x8*)(size_t)(xl + k_off<64>(wm * 64 + mi * 32 + l32, 2 * ks + hf));
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ni], bfr[mi], acc[ni][mi], 0, 0, 0);
+    }
+    wait_vm<0>();
+    wg_barrier();
+  }
+
+  // epilogue: element i of acc[ni][mi] is column n0 + 128 wn + 32 ni +
+  // 8 (i>>2) + (i&3) + 4 hf of row m0 + 64 wm + 32 mi + l32
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int64_t m = m0 + wm * 64 + mi * 32 + l32;
+    if (m >= g.m) continue;
+    __bf16* crow = g.c + m * g.ldc;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * 128 + ni * 32 + 8 * q + 4 * hf;
+        if (n >= g.n) continue;
+        const bf16x4 bb = *(const bf16x4*)(g.bias + n);
+        bf16x4 out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = acc[ni][mi][4 * q + j] + (float)bb[j];
+          if (GELU) v = gelu_tanh(v);
+          out[j] = (__bf16)v;
+        }
+        *(bf16x4*)(crow + n) = out;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t s) {
+  static bool attr_done = false;  // the attribute is idempotent
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bt_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)gemm_bt_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, G_LDS);
+    if (e != hipSuccess) return e;
+    attr_done = true;
+  }
+  const int64_t work = ((g.m + GBM - 1) / GBM) * ((g.n + GBN - 1) / GBN);
+  if (work == 0 || g.k == 0) return hipSuccess;
+  const dim3 grid((unsigned)(((work + 7) / 8) * 8));
+  if (g.gelu)
+    hipLaunchKernelGGL(gemm_bt_kernel<true>, grid, dim3(kGThreads), G_LDS, s, g);
+  else
+    hipLaunchKernelGGL(gemm_bt_kernel<false>, grid, dim3(kGThreads), G_LDS, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace ra

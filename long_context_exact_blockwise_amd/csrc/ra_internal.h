@@ -64,6 +64,22 @@ struct BwdArgs {
   float scale;
 };
 
+// One layer of the blockwise feedforward: C[M, N] = A[M, K] B[N, K]^T +
+// bias[N] (then GELU when gelu != 0); bf16, row strides in elements, K a
+// multiple of 64.
+struct GemmArgs {
+  const __bf16* a;
+  int64_t lda;
+  const __bf16* b;
+  int64_t ldb;
+  const __bf16* bias;
+  __bf16* c;
+  int64_t ldc;
+  int64_t m;
+  int32_t n, k;
+  int32_t gelu;
+};
+
 // Launchers: validate nothing (the API layer did), enqueue, return the launch
 // error (hipSuccess on success).
 hipError_t launch_attn_bf16(const AttnArgs& a, const BlockTable& t, int mode, hipStream_t s);
@@ -75,5 +91,6 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s)
 hipError_t launch_bwd_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t s);
 hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, hipStream_t s);
+hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t s);
 
 }  // namespace ra

@@ -563,6 +563,48 @@ ra_status ringattn_ring_bwd(const ra_desc* desc, const void* q, const void* cons
   return RA_OK;
 }
 
+ra_status ringattn_ffn_fwd(const ra_ffn_desc* d, const void* x, const void* w1, const void* b1, const void* w2,
+                           const void* b2, void* y, void* workspace, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if (!d) return fail(RA_E_NULL, "desc is NULL");
+  if (d->rows < 0 || d->d_model <= 0 || d->d_ff <= 0)
+    return fail(RA_E_SHAPE, "rows (%lld) must be >= 0, d_model (%d) and d_ff (%d) > 0", (long long)d->rows,
+                d->d_model, d->d_ff);
+  if (d->d_model % 64 || d->d_ff % 64)
+    return fail(RA_E_UNSUPPORTED, "d_model (%d) and d_ff (%d) must be multiples of 64", d->d_model, d->d_ff);
+  if (d->d_model > 16384 || d->d_ff > 65536)
+    return fail(RA_E_UNSUPPORTED, "d_model <= 16384 and d_ff <= 65536 (got %d, %d)", d->d_model, d->d_ff);
+  if (d->x_stride < d->d_model || d->y_stride < d->d_model)
+    return fail(RA_E_SHAPE, "x_stride (%lld) and y_stride (%lld) must be >= d_model", (long long)d->x_stride,
+                (long long)d->y_stride);
+  if (d->x_stride % 8 || d->y_stride % 8)
+    return fail(RA_E_ALIGN, "x_stride and y_stride must be multiples of 8 elements (16-byte rows)");
+  if (d->x_stride * 2 * 256 >= (int64_t)1 << 31)
+    return fail(RA_E_UNSUPPORTED, "x_stride too large (a 256-row tile must span < 2 GiB)");
+  if (d->rows == 0) return RA_OK;
+  if (d->block_rows <= 0) return fail(RA_E_SHAPE, "block_rows must be >= 1");
+  const void* ptrs[] = {x, w1, b1, w2, b2, y, workspace};
+  const char* names[] = {"x", "w1", "b1", "w2", "b2", "y", "workspace"};
+  for (int i = 0; i < 7; ++i)
+    if ((st = need_ptr(ptrs[i], names[i])) != RA_OK) return st;
+  for (int i = 0; i < 7; ++i)
+    if ((st = check_mem(ptrs[i], false, names[i])) != RA_OK) return st;
+  const int64_t rb = d->block_rows < d->rows ? d->block_rows : d->rows;
+  for (int64_t r0 = 0; r0 < d->rows; r0 += rb) {
+    const int64_t m = d->rows - r0 < rb ? d->rows - r0 : rb;
+    ra::GemmArgs g1{(const __bf16*)x + r0 * d->x_stride, d->x_stride, (const __bf16*)w1, d->d_model,
+                    (const __bf16*)b1, (__bf16*)workspace, d->d_ff, m, d->d_ff, d->d_model, 1};
+    hipError_t e = ra::launch_gemm_bt(g1, stream);
+    if (e != hipSuccess) return hip_fail(e, "feedforward layer 1 launch");
+    ra::GemmArgs g2{(const __bf16*)workspace, d->d_ff, (const __bf16*)w2, d->d_ff, (const __bf16*)b2,
+                    (__bf16*)y + r0 * d->y_stride, d->y_stride, m, d->d_model, d->d_ff, 0};
+    e = ra::launch_gemm_bt(g2, stream);
+    if (e != hipSuccess) return hip_fail(e, "feedforward layer 2 launch");
+  }
+  return RA_OK;
+}
+
 ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream) {
   g_err.clear();
   ra_status st;

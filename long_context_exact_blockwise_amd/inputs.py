@@ -115,6 +115,35 @@ def make_grad(wl: Workload, device="cpu", seed: int = 0) -> torch.Tensor:
     return do.to(torch_dtype(wl.dtype))
 
 
+@dataclasses.dataclass(frozen=True)
+class FfnWorkload:
+    name: str
+    rows: int
+    d_model: int
+    d_ff: int
+    block_rows: int
+
+
+# The feedforward of the 1.3B model's layer (hidden dim 2048, 4x expansion)
+# over the 128K-token chunk of a 512K sequence on 4 devices, in blocks of 16K
+# rows (a 256 MiB hidden activation per block instead of 2 GiB for the chunk).
+FFN_CONFIG = FfnWorkload("bf16 FFN rows131072 d2048 f8192 block16384", 131072, 2048, 8192, 16384)
+
+
+def make_ffn_inputs(rows: int, d_model: int, d_ff: int, device="cpu", seed: int = 0):
+    """x [rows, d] ~ N(0, 1); W1 [F, d] ~ N(0, 1/d); b1 [F] ~ N(0, 0.1^2);
+    W2 [d, F] ~ N(0, 1/F); b2 [d] ~ N(0, 0.1^2): fp32 randn in that order
+    from one seeded generator, scaled in fp32, rounded to bf16."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn((rows, d_model), generator=g, device=device, dtype=torch.float32)
+    w1 = torch.randn((d_ff, d_model), generator=g, device=device, dtype=torch.float32) / math.sqrt(d_model)
+    b1 = torch.randn((d_ff,), generator=g, device=device, dtype=torch.float32) * 0.1
+    w2 = torch.randn((d_model, d_ff), generator=g, device=device, dtype=torch.float32) / math.sqrt(d_ff)
+    b2 = torch.randn((d_model,), generator=g, device=device, dtype=torch.float32) * 0.1
+    return tuple(t.to(torch.bfloat16) for t in (x, w1, b1, w2, b2))
+
+
 def sample_rows(q_len: int, extra: int = 8, seed: int = 1):
     """Rows checked at full size: the first, the last and `extra` seeded rows."""
     import numpy as np

@@ -30,6 +30,7 @@ SYMBOLS = (
     "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
     "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
     "ringattn_ring_fwd", "ringattn_probe_copy", "ringattn_bwd_delta", "ringattn_block_bwd", "ringattn_ring_bwd",
+    "ringattn_ffn_fwd",
 )
 
 
@@ -47,6 +48,13 @@ class RaDesc(ctypes.Structure):
         ("out_dtype", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("kv_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
         ("pos_stride", ctypes.c_int64),
+    ]
+
+
+class RaFfnDesc(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("x_stride", ctypes.c_int64), ("y_stride", ctypes.c_int64), ("block_rows", ctypes.c_int64),
     ]
 
 
@@ -88,6 +96,8 @@ def lib():
     L.ringattn_bwd_delta.argtypes = [D, P, P, P, P]
     L.ringattn_block_bwd.restype = ctypes.c_int
     L.ringattn_block_bwd.argtypes = [D, P, P, P, ctypes.c_int64, P, P, P, P, P, P, P]
+    L.ringattn_ffn_fwd.restype = ctypes.c_int
+    L.ringattn_ffn_fwd.argtypes = [ctypes.POINTER(RaFfnDesc), P, P, P, P, P, P, P, P]
     L.ringattn_ring_bwd.restype = ctypes.c_int
     L.ringattn_ring_bwd.argtypes = [D, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(ctypes.c_int64),
                                     ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P, P, P, P,
@@ -281,4 +291,37 @@ def ring_backward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: S
     dv = [torch.zeros((b, ck, h, d), dtype=torch.float32, device=q.device) for _ in k_blocks]
     ringattn_ring_bwd(desc, q, k_blocks, v_blocks, kv_pos0, o, dout, lse, delta, dq, dk, dv, kv_valid=kv_valid)
     return dq, dk, dv
+
+
+# ---- blockwise feedforward ----
+
+def ringattn_ffn_fwd(desc: RaFfnDesc, x, w1, b1, w2, b2, y, workspace, stream=None):
+    _check(lib().ringattn_ffn_fwd(ctypes.byref(desc), _ptr(x), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2), _ptr(y),
+                                  _ptr(workspace), _stream(stream)))
+
+
+def ffn_desc(x: torch.Tensor, w1: torch.Tensor, y: Optional[torch.Tensor] = None, block_rows: int = 0) -> RaFfnDesc:
+    """Descriptor for x [rows, d_model] (row stride as given, unit column
+    stride) and W1 [d_ff, d_model]; block_rows 0 means all rows in one block."""
+    rows, d = x.shape
+    if x.stride(1) != 1 or (y is not None and y.stride(1) != 1):
+        raise ValueError("the feature axis must be contiguous")
+    desc = RaFfnDesc()
+    desc.rows, desc.d_model, desc.d_ff = rows, d, w1.shape[0]
+    desc.x_stride = x.stride(0)
+    desc.y_stride = y.stride(0) if y is not None else d
+    desc.block_rows = block_rows if block_rows > 0 else max(rows, 1)
+    return desc
+
+
+def ffn_forward(x: torch.Tensor, w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: torch.Tensor, *,
+                block_rows: int = 0, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y = gelu(x W1^T + b1) W2^T + b2 over row blocks (bf16).  Allocates y
+    and, unless given, the [block_rows, d_ff] workspace."""
+    y = torch.empty((x.shape[0], w2.shape[0]), dtype=x.dtype, device=x.device)
+    desc = ffn_desc(x, w1, y, block_rows)
+    if workspace is None:
+        workspace = torch.empty((desc.block_rows, desc.d_ff), dtype=x.dtype, device=x.device)
+    ringattn_ffn_fwd(desc, x, w1, b1, w2, b2, y, workspace, stream=stream)
+    return y
 

@@ -41,7 +41,7 @@ def blockwise_ffn(x, w1, b1, w2, b2, block_rows: int | None = None):
     b2 = np.asarray(b2, dtype=np.float64)
     n = x.shape[0]
     step = n if not block_rows else int(block_rows)
-    y = np.empty((n, w2.shape[0]), dtype=np.float64)
+    y = np.full((n, w2.shape[0]), np.nan)  # a row no block writes stays NaN
     for r0 in range(0, n, max(step, 1)):
         h = gelu_tanh(x[r0:r0 + step] @ w1.T + b1)
         y[r0:r0 + step] = h @ w2.T + b2

@@ -216,3 +216,36 @@ def test_backward_checks_before_enqueue():
     assert L.ringattn_bwd_delta(ctypes.byref(d), FAKE, FAKE, FAKE + 2, None) == ra.RA_E_ALIGN
     d32 = _desc(in_dtype=ra.RA_F32, out_dtype=ra.RA_F32)
     assert L.ringattn_bwd_delta(ctypes.byref(d32), FAKE, FAKE, FAKE, None) == ra.RA_E_UNSUPPORTED
+
+
+def _ffn(**kw):
+    d = ra.RaFfnDesc()
+    d.rows, d.d_model, d.d_ff = kw.get("rows", 256), kw.get("d_model", 128), kw.get("d_ff", 512)
+    d.x_stride, d.y_stride = kw.get("x_stride", d.d_model), kw.get("y_stride", d.d_model)
+    d.block_rows = kw.get("block_rows", 128)
+    ptrs = kw.get("ptrs", [FAKE] * 7)
+    st = ra.lib().ringattn_ffn_fwd(ctypes.byref(d), *ptrs, None)
+    return st, ra.lib().ringattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), ra.RA_E_SHAPE),
+    (dict(d_model=0), ra.RA_E_SHAPE),
+    (dict(d_model=96), ra.RA_E_UNSUPPORTED),
+    (dict(d_ff=100), ra.RA_E_UNSUPPORTED),
+    (dict(d_ff=1 << 17), ra.RA_E_UNSUPPORTED),
+    (dict(x_stride=64), ra.RA_E_SHAPE),
+    (dict(y_stride=132), ra.RA_E_ALIGN),
+    (dict(x_stride=1 << 22), ra.RA_E_UNSUPPORTED),
+    (dict(block_rows=0), ra.RA_E_SHAPE),
+    (dict(ptrs=[FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE]), ra.RA_E_NULL),
+    (dict(ptrs=[FAKE, FAKE, FAKE, FAKE, FAKE + 8, FAKE, FAKE]), ra.RA_E_ALIGN),
+])
+def test_ffn_checks_before_enqueue(kw, status):
+    st, msg = _ffn(**kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def test_ffn_empty_chunk_needs_no_pointers():
+    assert _ffn(rows=0, ptrs=[None] * 7)[0] == ra.RA_OK
