@@ -22,7 +22,12 @@
 namespace ra {
 namespace {
 
-constexpr int kGWaves = 8;
+#ifndef RA_FFN_WM
+#define RA_FFN_WM 2
+#endif
+constexpr int WTN = 4;                            // 32-column products per wave (128 columns)
+constexpr int WTM = RA_FFN_WM;                    // 32-row products per wave
+constexpr int kGWaves = (256 / (32 * WTN)) * (256 / (32 * WTM));
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int GBM = 256;                          // rows of C per workgroup
 constexpr int GBN = 256;                          // columns of C per workgroup
@@ -32,14 +37,16 @@ constexpr int G_STAGE = 2 * G_TILE;               // weights tile, then token ti
 constexpr int G_LDS = 2 * G_STAGE;                // two stages: 128 KiB
 constexpr int G_CPW = G_STAGE / 1024 / kGWaves;   // 1 KiB copies per wave per stage
 
-// GELU, tanh form (Hendrycks and Gimpel): 0.5 x (1 + tanh(sqrt(2/pi) (x +
-// 0.044715 x^3))), with tanh(u) = 1 - 2 / (1 + e^(2u)) (exact at both
-// saturations: e^(2u) -> inf gives 1, -> 0 gives -1).
+// GELU, tanh form (Hendrycks and Gimpel): 0.5 x (1 + tanh(u)) with u =
+// sqrt(2/pi) (x + 0.044715 x^3), evaluated as x / (1 + e^(-2u)) (the same
+// function, since 0.5 (1 + tanh(u)) = 1 / (1 + e^(-2u))), with e^(-2u) =
+// 2^(x (c1 + c2 x^2)); both saturations are exact (e^(-2u) -> inf gives -0,
+// -> 0 gives x).
 __device__ __forceinline__ float gelu_tanh(float x) {
-  const float u = 0.7978845608028654f * __builtin_fmaf(0.044715f * x, x * x, x);
-  const float e = __builtin_amdgcn_exp2f(2.f * kLog2e * u);
-  const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(1.f + e);
-  return 0.5f * x * (1.f + t);
+  constexpr float c1 = -2.0f * 1.4426950408889634f * 0.7978845608028654f;  // -2 log2(e) sqrt(2/pi)
+  constexpr float c2 = c1 * 0.044715f;
+  const float e = __builtin_amdgcn_exp2f(x * __builtin_fmaf(c2, x * x, c1));
+  return x * __builtin_amdgcn_rcpf(1.f + e);
 }
 
 template <bool GELU>
@@ -54,14 +61,25 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
   // tile against a run of weight tiles
   const int64_t wid = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (wid >= n_work) return;
-  const int64_t tm = wid / tiles_n;
-  const int tn = (int)(wid - tm * tiles_n);
+#ifndef RA_FFN_GM
+#define RA_FFN_GM 4
+#endif
+  // tiles in groups of GM row tiles: consecutive ids walk GM row tiles, then
+  // the next column tile, so the workgroups that run together on one XCD
+  // share GM token tiles and a few weight tiles in its L2
+  const int64_t gspan = (int64_t)RA_FFN_GM * tiles_n;
+  const int64_t grp = wid / gspan;
+  const int64_t first_m = grp * RA_FFN_GM;
+  const int gsize = (int)(tiles_m - first_m < RA_FFN_GM ? tiles_m - first_m : RA_FFN_GM);
+  const int64_t in_g = wid - grp * gspan;
+  const int64_t tm = first_m + in_g % gsize;
+  const int tn = (int)(in_g / gsize);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
   const int wn = wave & 1;   // 128-column half of the tile
-  const int wm = wave >> 1;  // 64-row quarter of the tile
+  const int wm = wave >> 1;  // (32 WTM)-row slice of the tile
 
   const int64_t m0 = tm * GBM;
   const int n0 = tn * GBN;
@@ -94,11 +112,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[WTN][WTM];
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni)
+  for (int ni = 0; ni < WTN; ++ni)
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) acc[ni][mi] = f32x16{};
+    for (int mi = 0; mi < WTM; ++mi) acc[ni][mi] = f32x16{};
 
   issue(0);
   wait_vm<0>();
@@ -109,46 +127,77 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
     const uint32_t xl = wl + G_TILE;
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 af[4], bfr[2];
+      bf16x8 af[WTN], bfr[WTM];
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < WTN; ++ni)
         af[ni] = *(lds_bf16x8*)(size_t)(wl + k_off<64>(wn * 128 + ni * 32 + l32, 2 * ks + hf));
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        bfr[mi] = *(lds_bf16x8*)(size_t)(xl + k_off<64>(wm * 64 + mi * 32 + l32, 2 * ks + hf));
+      for (int mi = 0; mi < WTM; ++mi)
+        bfr[mi] = *(lds_bf16x8*)(size_t)(xl + k_off<64>(wm * 32 * WTM + mi * 32 + l32, 2 * ks + hf));
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < WTN; ++ni)
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < WTM; ++mi)
           acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ni], bfr[mi], acc[ni][mi], 0, 0, 0);
     }
+#ifdef RA_FFN_IGLP
+    __builtin_amdgcn_iglp_opt(RA_FFN_IGLP);
+#endif
     wait_vm<0>();
     wg_barrier();
   }
 
   // epilogue: element i of acc[ni][mi] is column n0 + 128 wn + 32 ni +
-  // 8 (i>>2) + (i&3) + 4 hf of row m0 + 64 wm + 32 mi + l32
+  // 8 (i>>2) + (i&3) + 4 hf of row m0 + 32 WTM wm + 32 mi + l32.  After bias
+  // (and GELU) and the bf16 rounding, the two lanes of a row (hf = 0, 1)
+  // trade halves with permlane32 swaps so that each holds 8 consecutive
+  // columns per store: hf 0 columns 8q..8q+7 for q = 0, 1; hf 1 for q = 2, 3.
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int64_t m = m0 + wm * 64 + mi * 32 + l32;
-    if (m >= g.m) continue;
-    __bf16* crow = g.c + m * g.ldc;
+  for (int mi = 0; mi < WTM; ++mi) {
+    const int64_t m = m0 + wm * 32 * WTM + mi * 32 + l32;
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int ni = 0; ni < WTN; ++ni) {
+      const int nb = n0 + wn * 128 + ni * 32;  // N is a multiple of 64: a 32-column group is all in or all out
+      if (nb >= g.n) continue;
+      uint32_t d[4][2];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * 128 + ni * 32 + 8 * q + 4 * hf;
-        if (n >= g.n) continue;
-        const bf16x4 bb = *(const bf16x4*)(g.bias + n);
-        bf16x4 out;
+        const bf16x4 bb = *(const bf16x4*)(g.bias + nb + 8 * q + 4 * hf);
+        float v[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float v = acc[ni][mi][4 * q + j] + (float)bb[j];
-          if (GELU) v = gelu_tanh(v);
-          out[j] = (__bf16)v;
+          v[j] = acc[ni][mi][4 * q + j] + (float)bb[j];
+          if (GELU) v[j] = gelu_tanh(v[j]);
         }
-        *(bf16x4*)(crow + n) = out;
+        const bf16x2 lo = {(__bf16)v[0], (__bf16)v[1]};
+        const bf16x2 hi = {(__bf16)v[2], (__bf16)v[3]};
+        d[q][0] = __builtin_bit_cast(uint32_t, lo);
+        d[q][1] = __builtin_bit_cast(uint32_t, hi);
       }
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          // (vdst = group q, vsrc = group q+2; the upper lanes of vdst trade
+          // with the lower lanes of vsrc): lanes 0-31 end with their own q
+          // in d[q] and the upper lanes' q in d[q+2]; lanes 32-63 with the
+          // lower lanes' q+2 in d[q] and their own q+2 in d[q+2]
+          const auto r = __builtin_amdgcn_permlane32_swap(d[q][h2], d[q + 2][h2], false, false);
+          d[q][h2] = r[0];
+          d[q + 2][h2] = r[1];
+        }
+      if (m < g.m) {
+        __bf16* crow = g.c + m * g.ldc + nb;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int qq = hf ? q + 2 : q;
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          // columns 8 qq + 0..3 sit in d[q], 8 qq + 4..7 in d[q+2], on both halves
+          const u32x4 w = u32x4{d[q][0], d[q][1], d[q + 2][0], d[q + 2][1]};
+          *(u32x4*)(crow + 8 * qq) = w;
+        }
+      }
+    }
   }
 }
 
