@@ -11,14 +11,15 @@
 // block it receives, its contribution to that block's dK and dV, which in the
 // ring travel on with the block.  All three are accumulated (+=) in fp32.
 //
-// Two kernels per block, eight waves per workgroup (two per SIMD, so one
-// wave's MFMAs overlap the other's exponentials, LDS reads and barrier), each
+// Two kernels per block, eight or twelve waves per workgroup (two or three
+// per SIMD, so one wave's MFMAs overlap another's exponentials, LDS reads and
+// barrier), each
 // streaming tiles through a three-stage LDS ring of direct global->LDS copies
 // (the copy of tile t+2 is in flight while tile t is computed):
 //   dq kernel:   a workgroup owns 256 query rows (32 per wave) and streams
 //                the block's 64-key tiles: S^T = K Q^T, dP^T = V dO^T, then
 //                dQ^T += K^T dS^T.  Q and dO fragments stay in registers.
-//   dkdv kernel: a workgroup owns 256 keys (32 per wave; K (and V)
+//   dkdv kernel: a workgroup owns 32 keys per wave (K (and V)
 //                fragments in registers) and streams 32-row query tiles, with
 //                the tile's LSE (and delta) copied into LDS beside Q and dO,
 //                in two passes that each fit two waves per SIMD: S = Q K^T,
@@ -35,11 +36,17 @@
 namespace ra {
 namespace {
 
-constexpr int kBWaves = 8;                 // waves per workgroup in both kernels
+constexpr int kBWaves = 8;                 // waves per workgroup of the dq kernel
 constexpr int kBThreads = 64 * kBWaves;
 constexpr int BQ = 32 * kBWaves;           // dq kernel: query rows per workgroup
 constexpr int BKN = 64;                    // dq kernel: keys per tile
-constexpr int BKK = 32 * kBWaves;          // dkdv kernel: keys per workgroup
+#ifndef RA_DV_WAVES
+#define RA_DV_WAVES 12
+#endif
+// dkdv kernel: waves per workgroup of each pass (32 keys per wave); the dV
+// pass needs fewer registers and may run more waves per SIMD
+template <int PASS>
+constexpr int kv_waves() { return PASS == 0 ? RA_DV_WAVES : 8; }
 constexpr int BQT = 32;                    // dkdv kernel: query rows per tile
 constexpr int kStages = 3;                 // LDS ring depth
 
@@ -280,6 +287,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
 // delta) and accumulates dK^T += Q^T dS.
 template <int D, int PASS>
 struct KvStage {
+  static constexpr int NW = kv_waves<PASS>();
+  static constexpr int BKK = 32 * NW;                            // keys per workgroup
   static constexpr int QT = BQT * D * 2;
   static constexpr int NCOPY = PASS == 0 ? 2 : 3;   // PASS 0: Q rows, dO^T; PASS 1: Q rows, dO rows, Q^T
   static constexpr int TR_MASK = PASS == 0 ? 0b10 : 0b100;
@@ -288,14 +297,15 @@ struct KvStage {
   static constexpr int BYTES = NCOPY * QT + (PASS == 0 ? 256 : 512);
   static constexpr int LDS = kStages * BYTES;
   static constexpr int TOTAL = NCOPY * QT / 1024;                 // 1 KiB copies per tile
-  static constexpr int CPW = (TOTAL + kBWaves - 1) / kBWaves;     // per wave (the last round may repeat a copy)
+  static constexpr int CPW = (TOTAL + NW - 1) / NW;               // per wave (the last round may repeat a copy)
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 template <int D, int PASS>
-__global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<D>;
   using S = KvStage<D, PASS>;
+  constexpr int BKK = S::BKK;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int n_kt = (int)((a.kv_len + BKK - 1) / BKK);
   const int n_work = a.batch * a.heads * n_kt;
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
     const int per_copy = S::QT / 1024;
 #pragma unroll
     for (int j = 0; j < S::CPW; ++j) {
-      int g = wave + kBWaves * j;
+      int g = wave + S::NW * j;
       if (g >= S::TOTAL) g -= S::TOTAL;  // repeat a copy another wave makes (same bytes, same place)
       const int cp = g / per_copy;
       const int cc = g - cp * per_copy;
@@ -476,18 +486,20 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
     attr_done = true;
   }
   const int64_t nq = (int64_t)a.batch * a.heads * ((a.q_len + BQ - 1) / BQ);
-  const int64_t nk = (int64_t)a.batch * a.heads * ((a.kv_len + BKK - 1) / BKK);
+  const int64_t nk0 = (int64_t)a.batch * a.heads * ((a.kv_len + KvStage<D, 0>::BKK - 1) / KvStage<D, 0>::BKK);
+  const int64_t nk1 = (int64_t)a.batch * a.heads * ((a.kv_len + KvStage<D, 1>::BKK - 1) / KvStage<D, 1>::BKK);
   if (nq > 0) {
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(((nq + 7) / 8) * 8)), dim3(kBThreads), C::DQ_LDS, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (nk > 0) {
-    const dim3 grid((unsigned)(((nk + 7) / 8) * 8));
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 0>), grid, dim3(kBThreads), (KvStage<D, 0>::LDS), s, a);
+  if (nk0 > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 0>), dim3((unsigned)(((nk0 + 7) / 8) * 8)),
+                       dim3(64 * KvStage<D, 0>::NW), (KvStage<D, 0>::LDS), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), grid, dim3(kBThreads), (KvStage<D, 1>::LDS), s, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), dim3((unsigned)(((nk1 + 7) / 8) * 8)),
+                       dim3(64 * KvStage<D, 1>::NW), (KvStage<D, 1>::LDS), s, a);
   }
   return hipGetLastError();
 }
