@@ -118,31 +118,44 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
 #pragma unroll
     for (int mi = 0; mi < WTM; ++mi) acc[ni][mi] = f32x16{};
 
+  // per-lane byte offsets of this wave's operand rows for k-step ks (first
+  // 32-row group; each further group is 4 KiB on, an instruction immediate:
+  // the chunk XOR of k_off depends on the row only through bits 1..3)
+  uint32_t aoff[GBK / 16], boff[GBK / 16];
+#pragma unroll
+  for (int ks = 0; ks < GBK / 16; ++ks) {
+    aoff[ks] = (uint32_t)k_off<64>(wn * 128 + l32, 2 * ks + hf);
+    boff[ks] = (uint32_t)(G_TILE + k_off<64>(wm * 32 * WTM + l32, 2 * ks + hf));
+  }
+
   issue(0);
   wait_vm<0>();
   wg_barrier();
   for (int kt = 0; kt < nk; ++kt) {
     if (kt + 1 < nk) issue(kt + 1);
-    const uint32_t wl = base + (kt & 1) * G_STAGE;
-    const uint32_t xl = wl + G_TILE;
+    const uint32_t sb = base + (kt & 1) * G_STAGE;
+    // operands of k-step ks+1 are read while the products of k-step ks run
+    bf16x8 af[2][WTN], bfr[2][WTM];
+    auto load = [&](int buf, int ks) {
+#pragma unroll
+      for (int ni = 0; ni < WTN; ++ni) af[buf][ni] = *(lds_bf16x8*)(size_t)(sb + aoff[ks] + ni * 4096);
+#pragma unroll
+      for (int mi = 0; mi < WTM; ++mi) bfr[buf][mi] = *(lds_bf16x8*)(size_t)(sb + boff[ks] + mi * 4096);
+    };
+    load(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
-      bf16x8 af[WTN], bfr[WTM];
-#pragma unroll
-      for (int ni = 0; ni < WTN; ++ni)
-        af[ni] = *(lds_bf16x8*)(size_t)(wl + k_off<64>(wn * 128 + ni * 32 + l32, 2 * ks + hf));
-#pragma unroll
-      for (int mi = 0; mi < WTM; ++mi)
-        bfr[mi] = *(lds_bf16x8*)(size_t)(xl + k_off<64>(wm * 32 * WTM + mi * 32 + l32, 2 * ks + hf));
+      const int cur = ks & 1;
+      if (ks + 1 < GBK / 16) load(cur ^ 1, ks + 1);  // issued before this step's products
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ni = 0; ni < WTN; ++ni)
 #pragma unroll
         for (int mi = 0; mi < WTM; ++mi)
-          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ni], bfr[mi], acc[ni][mi], 0, 0, 0);
+          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][ni], bfr[cur][mi], acc[ni][mi], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-#ifdef RA_FFN_IGLP
-    __builtin_amdgcn_iglp_opt(RA_FFN_IGLP);
-#endif
     wait_vm<0>();
     wg_barrier();
   }
