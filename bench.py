@@ -102,6 +102,29 @@ def read_traffic():
         return None
 
 
+def probe_peak(dev, iters: int = 200000, reps: int = 2) -> float:
+    """bf16 MFMA rate the part sustains under load (TFLOP/s): the library's
+    MFMA-only probe on every CU (four 512-thread groups per CU, four waves per
+    SIMD, ~50 ms per launch), best of `reps`."""
+    import torch
+    from long_context_exact_blockwise_amd import ringattn as ra
+    wgs = 4 * 256
+    out = torch.empty(wgs * ra.PROBE_THREADS, dtype=torch.float32, device=dev)
+    ra.ringattn_probe_mfma(out, wgs, 1000)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ra.ringattn_probe_mfma(out, wgs, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        f = wgs * (ra.PROBE_THREADS // 64) * iters * ra.PROBE_FLOP_PER_ITER_PER_WAVE
+        best = max(best, f / (ms * 1e-3) / 1e12)
+    return best
+
+
 def bwd_flops(wl) -> int:
     return 10 * wl.batch * wl.heads * wl.head_dim * visible_pairs(wl)
 
@@ -396,6 +419,8 @@ def main():
                     "copy-only rate",
         }
 
+    probed = probe_peak(dev) if wl.dtype == "bf16" else None
+
     if args.traffic_calib:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -411,6 +436,10 @@ def main():
         "kernel": "attn_bf16_kernel (fused ring pass)" if not perblock else "attn_bf16_kernel (per block)",
         "launches_per_step": 1 if (not perblock and len(kb) <= ra.RA_FUSED_MAX_BLOCKS) else None,
         "algorithmic_flop_per_step": f,
+        "probed_peak": probed,
+        "frac_of_probed": (achieved / probed) if probed else None,
+        "probed_peak_note": "bf16 MFMA rate measured on this part under load by ringattn_probe_mfma "
+                            "(MFMA-only kernel on every CU); peak is the published 2.5 PF figure",
     }
     if wl.dtype != "bf16":
         roofline.update(bound="latency", peak=None, frac=None)
@@ -426,6 +455,7 @@ def main():
             ("per-block" if perblock else "fused"),
         },
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "pct_of_probed_peak": (100.0 * value / probed) if probed else None,
         "kernel_ms": kern_ms,
         "roofline": roofline,
         "outputs_finite": finite,
@@ -443,8 +473,12 @@ def main():
     if not args.no_backward and wl.dtype == "bf16" and not wl.host_streamed:
         heads = [0, wl.heads - 1]
         result["backward"] = backward_measure(x, wl, kb, vb, pos, o, lse, args.bwd_steps, 1, heads)
+        if probed:
+            result["backward"]["pct_of_probed_peak"] = 100.0 * result["backward"]["value"] / probed
     if not args.no_ffn:
         result["ffn"] = ffn_measure(dev, 10, 2)
+        if probed:
+            result["ffn"]["pct_of_probed_peak"] = 100.0 * result["ffn"]["value"] / probed
     print(json.dumps(result), flush=True)
 
 

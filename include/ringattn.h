@@ -248,6 +248,14 @@ ra_status ringattn_ffn_fwd(const ra_ffn_desc* desc, const void* x, const void* w
  * calibrate hardware byte counters and HBM bandwidth. */
 ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t stream);
 
+/* Measurement helper, not part of the attention path: `workgroups` groups of
+ * 512 threads each issue 4 * iters back-to-back bf16 MFMA products
+ * (v_mfma_f32_32x32x16_bf16, 32768 flop each) with no memory traffic, then
+ * write one float per thread to `out` (device memory, workgroups * 512
+ * floats).  Timed by the caller, it measures the bf16 MFMA rate the part
+ * sustains under load. */
+ra_status ringattn_probe_mfma(float* out, int32_t workgroups, int32_t iters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libringattn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["ringattn_api.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "ffn_bf16.hip", "state.hip"]
+SOURCES = ["ringattn_api.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "ffn_bf16.hip", "probe.hip", "state.hip"]
 
 
 def hipcc() -> str:

@@ -373,7 +373,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     // of those 4 rows.  Rows 4*(g>>1) + t (+8 for the second load, +16 per
     // key step, +32 per key block), columns 32db + 16*(g&1) + 4s: vofs[db].
     // Row offsets of 16 and 32 rows are multiples of DPW KiB, which the slot
-    // layout doubles; 8 rows is C::HI8.  All are instruction immediates.
+    // layout doubles; 8 rows is C::HI8.  Each tile forms the per-lane bases
+    // slot + kofs[ks] and slot + vofs[db] once; the row offsets are
+    // instruction immediates on top of them.
     int kofs[C::KS], vofs[C::DB];
     {
       const int kA = k_off<D>(l32, hf);
@@ -387,16 +389,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) vofs[db] = C::v_at(vA ^ (64 * db));
     }
-    auto k_frag = [&](uint32_t sl, int ks, int kb) -> bf16x8 {
-      return *(lds_bf16x8*)(size_t)(sl + kofs[ks] + 2 * kb * 32 * ROWB);
-    };
-    auto v_frag = [&](uint32_t sl, int db, int row) -> bf16x8 {
-      const uint32_t va = sl + vofs[db] + 2 * row * ROWB;
-      // (Assembled with a shuffle of two bf16x4 loads: building the fragment
-      // element by element from bit-cast 16-bit integers is miscompiled by
-      // this toolchain, which drops half the elements.)
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)va);
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(va + C::HI8));
+    // V^T fragment at per-lane base `base` (slot + vofs[db]), key rows `row`..
+    // (Assembled with a shuffle of two bf16x4 loads: building the fragment
+    // element by element from bit-cast 16-bit integers is miscompiled by this
+    // toolchain, which drops half the elements.)
+    auto v_frag = [&](uint32_t base, int row) -> bf16x8 {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(base + 2 * row * ROWB));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(base + 2 * row * ROWB + C::HI8));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
@@ -406,14 +405,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     for (int q = 0; q < 16; ++q) p_prev[q] = bf16x2{(__bf16)0.0f, (__bf16)0.0f};
 
     auto qk_products = [&](uint32_t sl, f32x16 (&sn)[2]) {
+      // per-lane bases of this slot, once per tile; the second 32 keys are
+      // an instruction immediate
+      uint32_t kb_base[C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) kb_base[ks] = sl + kofs[ks];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k_frag(sl, ks, kb), qf[ks], ks == 0 ? f32x16{} : sn[kb],
-                                                           0, 0, 0);
+          sn[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              *(lds_bf16x8*)(size_t)(kb_base[ks] + 2 * kb * 32 * ROWB), qf[ks], ks == 0 ? f32x16{} : sn[kb], 0, 0, 0);
     };
     auto pv_products = [&](uint32_t sl, const bf16x2 (&pp)[16]) {
+      // per-lane bases of this slot, once per tile; rows are instruction
+      // immediates (at most 48 rows + 8 rows of one slot, < 64 KiB)
+      uint32_t vb[C::DB];
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) vb[db] = sl + vofs[db];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
           const bf16x8 pf = __builtin_shufflevector(p_lo, p_hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
           for (int db = 0; db < C::DB; ++db)
-            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(sl, db, 32 * kb + 16 * tp), pf, acc[db], 0, 0, 0);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vb[db], 32 * kb + 16 * tp), pf, acc[db], 0, 0, 0);
         }
     };
 

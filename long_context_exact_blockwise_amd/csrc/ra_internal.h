@@ -92,5 +92,6 @@ hipError_t launch_bwd_delta(const AttnArgs& a, const void* dout, float* delta, h
 hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, hipStream_t s);
 hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t s);
+hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t s);
 
 }  // namespace ra

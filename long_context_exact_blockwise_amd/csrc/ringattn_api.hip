@@ -617,4 +617,15 @@ ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStre
   return e == hipSuccess ? RA_OK : hip_fail(e, "copy launch");
 }
 
+ra_status ringattn_probe_mfma(float* out, int32_t workgroups, int32_t iters, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = need_ptr(out, "out")) != RA_OK) return st;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 24))
+    return fail(RA_E_SHAPE, "workgroups must be in [1, 65536] and iters in [1, 2^24]");
+  if ((st = check_mem(out, false, "out")) != RA_OK) return st;
+  hipError_t e = ra::launch_probe_mfma(out, workgroups, iters, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "probe launch");
+}
+
 }  // extern "C"

@@ -30,7 +30,7 @@ SYMBOLS = (
     "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
     "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
     "ringattn_ring_fwd", "ringattn_probe_copy", "ringattn_bwd_delta", "ringattn_block_bwd", "ringattn_ring_bwd",
-    "ringattn_ffn_fwd",
+    "ringattn_ffn_fwd", "ringattn_probe_mfma",
 )
 
 
@@ -96,6 +96,8 @@ def lib():
     L.ringattn_bwd_delta.argtypes = [D, P, P, P, P]
     L.ringattn_block_bwd.restype = ctypes.c_int
     L.ringattn_block_bwd.argtypes = [D, P, P, P, ctypes.c_int64, P, P, P, P, P, P, P]
+    L.ringattn_probe_mfma.restype = ctypes.c_int
+    L.ringattn_probe_mfma.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
     L.ringattn_ffn_fwd.restype = ctypes.c_int
     L.ringattn_ffn_fwd.argtypes = [ctypes.POINTER(RaFfnDesc), P, P, P, P, P, P, P, P]
     L.ringattn_ring_bwd.restype = ctypes.c_int
@@ -207,6 +209,14 @@ def ringattn_ring_fwd(desc: RaDesc, q, k_blocks: Sequence, v_blocks: Sequence, k
 
 def ringattn_probe_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None):
     _check(lib().ringattn_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+PROBE_THREADS = 512
+PROBE_FLOP_PER_ITER_PER_WAVE = 4 * 32768  # four 32x32x16 products
+
+
+def ringattn_probe_mfma(out: torch.Tensor, workgroups: int, iters: int, stream=None):
+    _check(lib().ringattn_probe_mfma(_ptr(out), workgroups, iters, _stream(stream)))
 
 
 # ---- convenience wrappers (allocation of outputs / workspace with torch) ----

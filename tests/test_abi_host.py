@@ -249,3 +249,11 @@ def test_ffn_checks_before_enqueue(kw, status):
 
 def test_ffn_empty_chunk_needs_no_pointers():
     assert _ffn(rows=0, ptrs=[None] * 7)[0] == ra.RA_OK
+
+
+def test_probe_mfma_checks_before_enqueue():
+    L = ra.lib()
+    assert L.ringattn_probe_mfma(None, 1, 1, None) == ra.RA_E_NULL
+    assert L.ringattn_probe_mfma(FAKE + 4, 1, 1, None) == ra.RA_E_ALIGN
+    assert L.ringattn_probe_mfma(FAKE, 0, 1, None) == ra.RA_E_SHAPE
+    assert L.ringattn_probe_mfma(FAKE, 1, 0, None) == ra.RA_E_SHAPE
