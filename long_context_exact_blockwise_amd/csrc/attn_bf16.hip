@@ -449,7 +449,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     seek(cs, 0);
     const int wrow0 = 32 * wave;    // this wave's first row, relative to the workgroup
     const int myrow = wrow0 + l32;  // this lane's row, relative to the workgroup
-    for (int t = 0; t < n_tiles; ++t) {
+    // One tile: S of tile t in sc (softmax now), S of t+1 into sn, P of t-1
+    // in pp (P.V now), P of t into pc.  The loop runs two tiles per trip
+    // with the register sets swapping roles, so no copies rotate them.
+    auto tile = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x2 (&pp)[16], bf16x2 (&pc)[16]) {
       copy_slot(t + kBufs);
       __builtin_amdgcn_sched_barrier(0);
       // mask keys past the block end and (causal) keys after this lane's row:
@@ -465,26 +468,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            if (32 * kb + 8 * (i >> 2) + (i & 3) >= thr) s_cur[kb][i] = -INFINITY;
+            if (32 * kb + 8 * (i >> 2) + (i & 3) >= thr) sc[kb][i] = -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
       // interleaved: P.V of tile t-1, S of tile t+1, softmax of tile t
       const float mref = m2 == -INFINITY ? 0.f : m2;
-      pv_products(slot_at(t + 1), p_prev);
-      qk_products(slot_at(t + 1), s_nxt);
-      float rs = softmax_exp(s_cur, c2s, mref, p_cur);
+      pv_products(slot_at(t + 1), pp);
+      qk_products(slot_at(t + 1), sn);
+      float rs = softmax_exp(sc, c2s, mref, pc);
       __builtin_amdgcn_iglp_opt(3);
       __builtin_amdgcn_sched_barrier(0);
-      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) rs = softmax_redo<C::DB>(s_cur, c2s, m2, lpart, acc, p_cur);
+      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) rs = softmax_redo<C::DB>(sc, c2s, m2, lpart, acc, pc);
       lpart += rs;
-      // slot t+2 (read by block t+1) has landed; kBufs-2 newer slots may fly
+      // slot t+2 (read by tile t+1) has landed; kBufs-2 newer slots may fly
       wait_vm<(kBufs - 2) * 2 * DPW>();
       wg_barrier();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) p_prev[q] = p_cur[q];
       step(cs, 0);
+    };
+    int t = 0;
+    for (; t + 1 < n_tiles; t += 2) {
+      tile(t, s_cur, s_nxt, p_prev, p_cur);
+      tile(t + 1, s_nxt, s_cur, p_cur, p_prev);
+    }
+    if (t < n_tiles) {
+      tile(t, s_cur, s_nxt, p_prev, p_cur);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) p_prev[q] = p_cur[q];  // the last tile's P, for the final P.V
     }
     // P.V of the last tile (slot n+1 holds V_{n-1})
     pv_products(slot_at(n_tiles + 1), p_prev);
