@@ -92,10 +92,12 @@ __device__ __forceinline__ void copy_stage(const char* const (&srcs)[NCOPY], int
 
 // Transpose-read fragment (the A operand of a product whose contraction runs
 // over tile rows): rows `row` + {key0, key0 + 8} (+0..3 across lane groups),
-// columns 32 db + ..., exactly as the forward kernel gathers V^T.
+// columns 32 db + ..., exactly as the forward kernel gathers V^T.  `base` is
+// the tile address plus this lane's offset for column block db, formed once
+// per tile, so the row offsets are instruction immediates.
 template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(uint32_t tile, int vA, int db, int row) {
-  const uint32_t va = tile + (vA ^ (64 * db)) + row * (D * 2);
+__device__ __forceinline__ bf16x8 tr_frag(uint32_t base, int row) {
+  const uint32_t va = base + row * (D * 2);  // base = tile + (vA ^ 64 db); rows become immediates
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)va);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(va + 8 * D * 2));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -249,7 +251,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each half's operands short-lived (register budget)
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T (bases formed per read: this kernel has no
+    // registers to hold four more per tile)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -257,8 +260,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
         const bf16x8 pf = pack8(dsp, 8 * kb + 4 * tp);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ktl, vA, db, 32 * kb + 16 * tp), pf, acc[db],
-                                                            0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ktl + (vA ^ (64 * db)), 32 * kb + 16 * tp), pf,
+                                                            acc[db], 0, 0, 0);
       }
     if (t + 2 < n_tiles)
       wait_vm<C::DQ_CPW>();  // tile t+1 landed; t+2 may still be in flight
@@ -410,10 +413,10 @@ __global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs
     f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
-      const int o = k_off<D>(l32, 2 * ks + hf);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(ql + o), kfr[ks], sc, 0, 0, 0);
+      const uint32_t qa = ql + k_off<D>(l32, 2 * ks + hf);  // dO rows: + QT, an immediate
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)qa, kfr[ks], sc, 0, 0, 0);
       if constexpr (PASS == 1)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(st + S::QT + o), vfr[ks], dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(qa + S::QT), vfr[ks], dp, 0, 0, 0);
     }
     // rows of this tile that see key c: [lo, hi)
     const int64_t row_t0 = (int64_t)t * BQT;
@@ -442,12 +445,15 @@ __global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs
     }
     // dV^T += dO^T P or dK^T += Q^T dS (contraction over the 32 rows in two
     // 16-row steps tp)
+    uint32_t tb[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) tb[db] = trl + (vA ^ (64 * db));
 #pragma unroll
     for (int tp = 0; tp < 2; ++tp) {
       const bf16x8 xf = pack8(x, 4 * tp);
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(trl, vA, db, 16 * tp), xf, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tb[db], 16 * tp), xf, acc[db], 0, 0, 0);
     }
     if (t + 2 < n_qt)
       wait_vm<S::CPW>();  // tile t+1 (and its LSE, delta) landed
