@@ -255,3 +255,25 @@ def test_full_size_backward_sampled():
         ek = float(sdk.abs().max() / mk)
         ev = float((sdv - sdo).abs().max() / mv)
         assert ek <= 1e-3 and ev <= 1e-3, (h, ek, ev)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_striped_with_valid_lengths_backward(d):
+    """Both extensions at once: striped positions (P = 4) and blocks of
+    unequal length with NaN in the padding."""
+    p, n = 4, 160
+    valid = [160, 97, 0, 64]
+    wl = small(d=d, q_len=n, kv_len=n, p=p, q_idx=2)
+    x = inputs.make_inputs(wl, cuda(), seed=110 + d)
+    do = inputs.make_grad(wl, cuda(), seed=111 + d)
+    _poison_padding(x, valid)
+    order = ra.ringattn_ring_order(2, p)
+    dq, dk, dv = _run(x, do, order, list(range(p)), 2, True, valid=valid, pos_stride=p)
+    rq, rk, rv = _oracle_bwd(x, do, 2, list(range(p)), True, valid=valid, pos_stride=p, blocks=order)
+    out = [_check(dq, rq, "dQ")]
+    for i, j in enumerate(order):
+        m = valid[j]
+        assert torch.count_nonzero(dk[i][:, m:]) == 0 and torch.count_nonzero(dv[i][:, m:]) == 0
+        out.append(_check(dk[i][:, :m], rk[i], f"dK block {j}"))
+        out.append(_check(dv[i][:, :m], rv[i], f"dV block {j}"))
+    print(out)
