@@ -39,3 +39,10 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode != 0 and "ONE GPU" in r.stderr
+
+
+def test_backward_flops_are_five_products():
+    # S, dP, dQ, dK, dV: 2*D flop per visible pair each
+    wl = inputs.CONFIGS[3]
+    assert bench.bwd_flops(wl) == 10 * 16 * 128 * 60_129_607_680
+    assert bench.bwd_flops(wl) * 2 == bench.flops(wl) * 5
