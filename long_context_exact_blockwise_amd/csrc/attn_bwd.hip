@@ -11,21 +11,22 @@
 // block it receives, its contribution to that block's dK and dV, which in the
 // ring travel on with the block.  All three are accumulated (+=) in fp32.
 //
-// Two kernels per block, eight or twelve waves per workgroup (two or three
-// per SIMD, so one wave's MFMAs overlap another's exponentials, LDS reads and
-// barrier), each
-// streaming tiles through a three-stage LDS ring of direct global->LDS copies
-// (the copy of tile t+2 is in flight while tile t is computed):
+// Two kernels per block, eight waves per workgroup (two per SIMD, so one
+// wave's MFMAs overlap another's exponentials, LDS reads and barrier), each
+// streaming query or key tiles through an LDS ring of direct global->LDS
+// copies (the copy of tile t+2 is in flight while tile t is computed):
 //   dq kernel:   a workgroup owns 256 query rows (32 per wave) and streams
 //                the block's 64-key tiles: S^T = K Q^T, dP^T = V dO^T, then
 //                dQ^T += K^T dS^T.  Q and dO fragments stay in registers.
-//   dkdv kernel: a workgroup owns 32 keys per wave (K (and V)
-//                fragments in registers) and streams 32-row query tiles, with
-//                the tile's LSE (and delta) copied into LDS beside Q and dO,
-//                in two passes that each fit two waves per SIMD: S = Q K^T,
-//                P, dV^T += dO^T P; then S, dP = dO V^T, dS, dK^T += Q^T dS.
-//                The second S costs 2 D flops per visible pair on top of the
-//                12 D of the five products plus the dq kernel's S and dP.
+//   dkdv kernel: a workgroup owns 128 keys, 32 per pair of waves on one
+//                SIMD, and streams 32-row query tiles with their LSE and
+//                delta.  One wave of the pair holds K fragments, forms
+//                S = Q K^T and P, accumulates dV^T += dO^T P and hands P over
+//                through LDS; the other holds V fragments and, one tile
+//                behind, forms dP = dO V^T, dS = P (dP - delta) and
+//                accumulates dK^T += Q^T dS.  S and dP are formed here and
+//                again in the dq kernel: 14 D flops per visible pair against
+//                the 10 D of the five products.
 // Matrix products use v_mfma_f32_32x32x16_bf16 with the same operand layouts
 // as the forward kernel: transposed-operand fragments (K^T, dO^T, Q^T) come
 // from LDS with ds_read_b64_tr_b16 in the 4-row-group key order that matches
@@ -40,15 +41,8 @@ constexpr int kBWaves = 8;                 // waves per workgroup of the dq kern
 constexpr int kBThreads = 64 * kBWaves;
 constexpr int BQ = 32 * kBWaves;           // dq kernel: query rows per workgroup
 constexpr int BKN = 64;                    // dq kernel: keys per tile
-#ifndef RA_DV_WAVES
-#define RA_DV_WAVES 12
-#endif
-// dkdv kernel: waves per workgroup of each pass (32 keys per wave); the dV
-// pass needs fewer registers and may run more waves per SIMD
-template <int PASS>
-constexpr int kv_waves() { return PASS == 0 ? RA_DV_WAVES : 8; }
 constexpr int BQT = 32;                    // dkdv kernel: query rows per tile
-constexpr int kStages = 3;                 // LDS ring depth
+constexpr int kStages = 3;                 // LDS ring depth of the dq kernel
 
 template <int D>
 struct BCfg {
@@ -283,34 +277,42 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup per BKK keys of one (b, h); this lane's key c (as the
-// column of the 32x32 products).  Two passes over the query tiles keep each
-// within two waves' register budget: PASS 0 forms S = Q K^T and P and
-// accumulates dV^T += dO^T P; PASS 1 forms S and dP = dO V^T, dS = P (dP -
-// delta) and accumulates dK^T += Q^T dS.
-template <int D, int PASS>
-struct KvStage {
-  static constexpr int NW = kv_waves<PASS>();
-  static constexpr int BKK = 32 * NW;                            // keys per workgroup
+// dK and dV in one pass, split over wave pairs: a workgroup owns 128 keys;
+// wave w (0-3, the P side) and wave w+4 (the dS side) share a SIMD and the
+// same 32 keys.  For query tile t the P side forms S = Q K^T and P (from the
+// forward's LSE), stores P as bf16 in LDS and accumulates dV^T += dO^T P; one
+// tile later the dS side forms dP = dO V^T, reads that P (the value dV used),
+// forms dS = P (dP - delta) and accumulates dK^T += Q^T dS.  Both sides hold
+// the same key in the same lane and the scores in the same accumulator
+// layout, so the hand-over is a plain per-lane copy.  Four LDS stages: tile
+// t (P side), t-1 (dS side), t+1 landed, t+2 in flight; two P buffers
+// alternate between trips.
+constexpr int kPairStages = 4;
+constexpr int BKP = 128;  // keys per workgroup (32 per wave pair)
+
+template <int D>
+struct PairStage {
   static constexpr int QT = BQT * D * 2;
-  static constexpr int NCOPY = PASS == 0 ? 2 : 3;   // PASS 0: Q rows, dO^T; PASS 1: Q rows, dO rows, Q^T
-  static constexpr int TR_MASK = PASS == 0 ? 0b10 : 0b100;
-  static constexpr int LSE_OFF = NCOPY * QT;
-  static constexpr int DLT_OFF = NCOPY * QT + 256;
-  static constexpr int BYTES = NCOPY * QT + (PASS == 0 ? 256 : 512);
-  static constexpr int LDS = kStages * BYTES;
-  static constexpr int TOTAL = NCOPY * QT / 1024;                 // 1 KiB copies per tile
-  static constexpr int CPW = (TOTAL + NW - 1) / NW;               // per wave (the last round may repeat a copy)
+  // Q rows, dO^T (transpose placement), dO rows, Q^T (transpose placement),
+  // then LSE and delta of the tile's 32 rows
+  static constexpr int LSE_OFF = 4 * QT;
+  static constexpr int DLT_OFF = 4 * QT + 256;
+  static constexpr int BYTES = 4 * QT + 512;
+  static constexpr int PX_OFF = kPairStages * BYTES;  // two P buffers: 4 pairs x 64 lanes x 32 bytes
+  static constexpr int PX_BYTES = 4 * 64 * 32;
+  static constexpr int LDS = PX_OFF + 2 * PX_BYTES;
+  static constexpr int TOTAL = 4 * QT / 1024;
+  static constexpr int CPW = TOTAL / kBWaves;
+  static_assert(TOTAL % kBWaves == 0, "copies per wave");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int PASS>
-__global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs a) {
+template <int D>
+__global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<D>;
-  using S = KvStage<D, PASS>;
-  constexpr int BKK = S::BKK;
+  using S = PairStage<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int n_kt = (int)((a.kv_len + BKK - 1) / BKK);
+  const int n_kt = (int)((a.kv_len + BKP - 1) / BKP);
   const int n_work = a.batch * a.heads * n_kt;
   const int per = (n_work + 7) >> 3;
   const int wid = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
@@ -320,14 +322,15 @@ __global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs
   const int b = bh / a.heads;
   const int h = bh - b * a.heads;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int role = wave >> 2;  // 0: S, P, dV; 1: dP, dS, dK
+  const int pair = wave & 3;
   const int lane = threadIdx.x & 63;
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
-  const int64_t k0 = (int64_t)kt * BKK;
-  const int64_t c = k0 + 32 * wave + l32;
+  const int64_t k0 = (int64_t)kt * BKP;
+  const int64_t c = k0 + 32 * pair + l32;
   const bool key_ok = c < a.kv_len;
-  // first query row that can see the workgroup's first key
   int64_t r_min = 0;
   if (a.causal) {
     r_min = a.kv_pos0 + k0 - a.q_pos0;
@@ -337,26 +340,23 @@ __global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs
   const int n_qt = (int)((a.q_len + BQT - 1) / BQT);
   const int qt0 = (int)(r_min / BQT);
 
-  bf16x8 kfr[C::KS], vfr[PASS == 1 ? C::KS : 1];
+  // K fragments (role 0) or V fragments (role 1) of this lane's key
+  bf16x8 fr[C::KS];
   {
-    const int64_t off = b * a.kv_sb + c * a.kv_ss + h * a.kv_sh + 8 * hf;
+    const __bf16* src = (const __bf16*)(role == 0 ? a.k : a.v) + b * a.kv_sb + c * a.kv_ss + h * a.kv_sh + 8 * hf;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       if (key_ok) {
-        kfr[ks] = *(const bf16x8*)((const __bf16*)a.k + off + 16 * ks);
-        if constexpr (PASS == 1) vfr[ks] = *(const bf16x8*)((const __bf16*)a.v + off + 16 * ks);
+        fr[ks] = *(const bf16x8*)(src + 16 * ks);
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          kfr[ks][j] = (__bf16)0.0f;
-          if constexpr (PASS == 1) vfr[ks][j] = (__bf16)0.0f;
-        }
+        for (int j = 0; j < 8; ++j) fr[ks][j] = (__bf16)0.0f;
       }
     }
   }
   wait_vm<0>();  // the register loads above, before any copy is in flight
   const float c2 = a.scale * kLog2e;
-  const int64_t first_row = a.causal ? a.kv_pos0 + c - a.q_pos0 : 0;  // first row (chunk-relative) seeing key c
+  const int64_t first_row = a.causal ? a.kv_pos0 + c - a.q_pos0 : 0;
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -367,34 +367,33 @@ __global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs
   const char* osrc = (const char*)a.dout + (b * a.q_sb + h * a.q_sh) * 2;
   const char* lse_bh = (const char*)(a.lse + ((int64_t)b * a.heads + h) * a.q_len);
   const char* dl_bh = (const char*)(a.delta + ((int64_t)b * a.heads + h) * a.q_len);
+  auto stage = [&](int t) -> uint32_t { return base + (t % kPairStages) * S::BYTES; };
   auto issue = [&](int t) {
-    const uint32_t st = base + (t % kStages) * S::BYTES;
+    const uint32_t st = stage(t);
     const int64_t row = (int64_t)t * BQT + l32;
     const uint32_t roff = (uint32_t)((row < a.q_len ? row : a.q_len - 1) * 4);
-    // waves 0 and 1 also copy the tile's LSE and delta (before the tiles, so
-    // the common vmcnt bound below covers them too)
     if (wave == 0) lds_dma4(lse_bh, roff, st + S::LSE_OFF);
-    if (PASS == 1 && wave == 1) lds_dma4(dl_bh, roff, st + S::DLT_OFF);
+    if (wave == 1) lds_dma4(dl_bh, roff, st + S::DLT_OFF);
     const int64_t go = (int64_t)t * BQT * qrow_bytes;
     const int valid = (int)(a.q_len - (int64_t)t * BQT);
     const int per_copy = S::QT / 1024;
 #pragma unroll
     for (int j = 0; j < S::CPW; ++j) {
-      int g = wave + S::NW * j;
-      if (g >= S::TOTAL) g -= S::TOTAL;  // repeat a copy another wave makes (same bytes, same place)
-      const int cp = g / per_copy;
+      const int g = wave + kBWaves * j;
+      const int cp = g / per_copy;  // 0: Q rows, 1: dO^T, 2: dO rows, 3: Q^T
       const int cc = g - cp * per_copy;
       const int p = cc * 1024 + lane * 16;
       const int rw = p / (D * 2);
       const int cs = (p % (D * 2)) / 16;
-      const bool tr = (S::TR_MASK >> cp) & 1;
-      const int col = (tr ? v_off<D>(rw, cs) : k_off<D>(rw, cs)) / 16 - rw * (D / 8);  // XOR is self-inverse
+      const bool tr = cp & 1;
+      const int col = (tr ? v_off<D>(rw, cs) : k_off<D>(rw, cs)) / 16 - rw * (D / 8);
       const int rr = rw < valid ? rw : valid - 1;
-      const char* src = cp == 1 ? osrc + go : qsrc + go;  // copy 1 is dO in both passes
+      const char* src = (cp == 1 || cp == 2) ? osrc + go : qsrc + go;
       lds_dma16(src, (uint32_t)(rr * qrow_bytes + col * 16), st + cp * S::QT + cc * 1024);
     }
   };
   const int vA = tr_base<D>(lane);
+  const uint32_t px_lane = base + S::PX_OFF + pair * (64 * 32) + lane * 32;  // this lane's 32 bytes of P
 
   issue(qt0);
   if (qt0 + 1 < n_qt) {
@@ -404,66 +403,90 @@ __global__ __launch_bounds__(64 * kv_waves<PASS>()) void bwd_dkdv_kernel(BwdArgs
     wait_vm<0>();
   }
   wg_barrier();
-  for (int t = qt0; t < n_qt; ++t) {
+  const int n_iter = n_qt - qt0 + 1;  // the last trip serves only the dK side
+  for (int i = 0; i < n_iter; ++i) {
+    const int t = qt0 + i;
     if (t + 2 < n_qt) issue(t + 2);
-    const uint32_t st = base + (t % kStages) * S::BYTES;
-    const uint32_t ql = st;                                       // Q rows
-    const uint32_t trl = st + (PASS == 0 ? 1 : 2) * S::QT;        // dO^T (PASS 0) or Q^T (PASS 1)
-    // S = Q K^T (and dP = dO V^T): rows the tile's 32 queries, columns keys
-    f32x16 sc = f32x16{}, dp = f32x16{};
+    const int tw = role == 0 ? t : t - 1;  // this wave's tile
+    if (tw >= qt0 && tw < n_qt) {
+      const uint32_t st = stage(tw);
+      const int64_t row_t0 = (int64_t)tw * BQT;
+      const int lo = key_ok ? clamp_i(first_row - row_t0, 0, BQT) : BQT;
+      const int hi = clamp_i(a.q_len - row_t0, 0, BQT);
+      // S = Q K^T (role 0) or dP = dO V^T (role 1)
+      f32x16 r = f32x16{};
+      const uint32_t rows = st + (role == 0 ? 0 : 2 * S::QT);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const uint32_t qa = ql + k_off<D>(l32, 2 * ks + hf);  // dO rows: + QT, an immediate
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)qa, kfr[ks], sc, 0, 0, 0);
-      if constexpr (PASS == 1)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(qa + S::QT), vfr[ks], dp, 0, 0, 0);
-    }
-    // rows of this tile that see key c: [lo, hi)
-    const int64_t row_t0 = (int64_t)t * BQT;
-    const int lo = key_ok ? clamp_i(first_row - row_t0, 0, BQT) : BQT;
-    const int hi = clamp_i(a.q_len - row_t0, 0, BQT);
-    // P = exp2(S c - LSE2[row]) (PASS 0) or dS = P (dP - delta[row]) (PASS 1),
-    // as bf16 pairs of consecutive elements (rows 8 (i>>2) + (i&3) + 4 hf)
-    bf16x2 x[8];
+      for (int ks = 0; ks < C::KS; ++ks)
+        r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rows + k_off<D>(l32, 2 * ks + hf)), fr[ks],
+                                                    r, 0, 0, 0);
+      bf16x2 x[8];
+      if (role == 0) {
+        // P = exp2(S c - LSE2[row]), masked; kept for the dK side
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
-      const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (8 * g + 4 * hf) * 4);
-      f32x4 d4 = f32x4{};
-      if constexpr (PASS == 1) d4 = *(lds_f32x4*)(size_t)(st + S::DLT_OFF + (8 * g + 4 * hf) * 4);
-      float v[4];
+        for (int g = 0; g < 4; ++g) {
+          typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+          const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (8 * g + 4 * hf) * 4);
+          float v[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * g + j;
-        const int row = acc_row(i, hf);
-        const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
-        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], c2, -l4[j] * kLog2e)) : 0.f;
-        v[j] = PASS == 0 ? p : p * (dp[i] - (vis ? d4[j] : 0.f));
+          for (int j = 0; j < 4; ++j) {
+            const int row = acc_row(4 * g + j, hf);
+            const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
+            v[j] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)) : 0.f;
+          }
+          x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+          x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
+        }
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+        const uint32_t px = px_lane + (i & 1) * S::PX_BYTES;
+        *(lds_u32x4*)(size_t)px = u32x4{__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
+                                        __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3])};
+        *(lds_u32x4*)(size_t)(px + 16) = u32x4{__builtin_bit_cast(uint32_t, x[4]), __builtin_bit_cast(uint32_t, x[5]),
+                                               __builtin_bit_cast(uint32_t, x[6]), __builtin_bit_cast(uint32_t, x[7])};
+      } else {
+        // dS = P (dP - delta[row]), P written by the pair's other wave last trip
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4c;
+        const uint32_t px = px_lane + ((i - 1) & 1) * S::PX_BYTES;
+        const u32x4 w0 = *(lds_u32x4c*)(size_t)px;
+        const u32x4 w1 = *(lds_u32x4c*)(size_t)(px + 16);
+        const uint32_t pw[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
+          const f32x4 d4 = *(lds_f32x4*)(size_t)(st + S::DLT_OFF + (8 * g + 4 * hf) * 4);
+          const bf16x2 pa = __builtin_bit_cast(bf16x2, pw[2 * g]);
+          const bf16x2 pb = __builtin_bit_cast(bf16x2, pw[2 * g + 1]);
+          const float pv[4] = {(float)pa[0], (float)pa[1], (float)pb[0], (float)pb[1]};
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = pv[j] * (r[4 * g + j] - d4[j]);
+          x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+          x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
+        }
       }
-      x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
-      x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
-    }
-    // dV^T += dO^T P or dK^T += Q^T dS (contraction over the 32 rows in two
-    // 16-row steps tp)
-    uint32_t tb[C::DB];
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1)
+      const uint32_t trl = st + (role == 0 ? S::QT : 3 * S::QT);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) tb[db] = trl + (vA ^ (64 * db));
+      for (int tp = 0; tp < 2; ++tp) {
+        const bf16x8 xf = pack8(x, 4 * tp);
 #pragma unroll
-    for (int tp = 0; tp < 2; ++tp) {
-      const bf16x8 xf = pack8(x, 4 * tp);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(tb[db], 16 * tp), xf, acc[db], 0, 0, 0);
+        for (int db = 0; db < C::DB; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(trl + (vA ^ (64 * db)), 16 * tp), xf, acc[db],
+                                                            0, 0, 0);
+      }
     }
     if (t + 2 < n_qt)
-      wait_vm<S::CPW>();  // tile t+1 (and its LSE, delta) landed
+      wait_vm<S::CPW>();  // tile t+1 landed; t+2 may be in flight
     else
       wait_vm<0>();
+    wait_lds();  // the P just written, before the other wave of the pair reads it
     wg_barrier();
   }
   if (!key_ok) return;
-  float* out = (PASS == 0 ? a.dv : a.dk) + (((int64_t)b * a.kv_cap + c) * a.heads + h) * D + 4 * hf;
-  const float f = PASS == 0 ? 1.f : a.scale;
+  float* out = (role == 0 ? a.dv : a.dk) + (((int64_t)b * a.kv_cap + c) * a.heads + h) * D + 4 * hf;
+  const float f = role == 0 ? 1.f : a.scale;
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -483,30 +506,21 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
     hipError_t e =
         hipFuncSetAttribute((const void*)bwd_dq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, C::DQ_LDS);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, 0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            KvStage<D, 0>::LDS);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            KvStage<D, 1>::LDS);
+    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            PairStage<D>::LDS);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const int64_t nq = (int64_t)a.batch * a.heads * ((a.q_len + BQ - 1) / BQ);
-  const int64_t nk0 = (int64_t)a.batch * a.heads * ((a.kv_len + KvStage<D, 0>::BKK - 1) / KvStage<D, 0>::BKK);
-  const int64_t nk1 = (int64_t)a.batch * a.heads * ((a.kv_len + KvStage<D, 1>::BKK - 1) / KvStage<D, 1>::BKK);
+  const int64_t nk = (int64_t)a.batch * a.heads * ((a.kv_len + BKP - 1) / BKP);
   if (nq > 0) {
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(((nq + 7) / 8) * 8)), dim3(kBThreads), C::DQ_LDS, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (nk0 > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 0>), dim3((unsigned)(((nk0 + 7) / 8) * 8)),
-                       dim3(64 * KvStage<D, 0>::NW), (KvStage<D, 0>::LDS), s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), dim3((unsigned)(((nk1 + 7) / 8) * 8)),
-                       dim3(64 * KvStage<D, 1>::NW), (KvStage<D, 1>::LDS), s, a);
-  }
+  if (nk > 0)
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(((nk + 7) / 8) * 8)), dim3(kBThreads), PairStage<D>::LDS,
+                       s, a);
   return hipGetLastError();
 }
 

@@ -101,6 +101,10 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0) with the other counters left alone: this wave's LDS
+// writes have landed (before a barrier that hands them to other waves).
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // Workgroup barrier without a memory fence: every wait a barrier needs here
 // is explicit (the copies' vmcnt; LDS reads are consumed before the barrier).
 __device__ __forceinline__ void wg_barrier() {
