@@ -422,17 +422,29 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
                                                     r, 0, 0, 0);
       bf16x2 x[8];
       if (role == 0) {
-        // P = exp2(S c - LSE2[row]), masked; kept for the dK side
+        // P = exp2(S c - LSE2[row]), masked; kept for the dK side.  Where
+        // every row of the tile sees every key of the wave (wave-uniform),
+        // no position test is needed, and exp2(-|x|) covers rows without a
+        // visible key: x = S c - LSE2 <= 0 for a row's visible keys (LSE is
+        // at least each visible score), while LSE = -inf makes x = +inf and
+        // P = 0; the sign and absolute value are free operand modifiers.
+        const bool full = hi == BQT && __all(lo == 0);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
           const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (8 * g + 4 * hf) * 4);
           float v[4];
+          if (full) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int row = acc_row(4 * g + j, hf);
-            const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
-            v[j] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)) : 0.f;
+            for (int j = 0; j < 4; ++j)
+              v[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)));
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = acc_row(4 * g + j, hf);
+              const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
+              v[j] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)) : 0.f;
+            }
           }
           x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
           x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
