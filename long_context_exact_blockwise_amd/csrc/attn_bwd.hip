@@ -219,6 +219,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
     const uint32_t ktl = kl + C::KT;
     const uint32_t vl = kl + 2 * C::KT;
     const int kv_rel = clamp_i(klim - (int64_t)t * BKN, 0, BKN);  // visible keys of this tile: [0, kv_rel)
+    const bool full = __all(kv_rel == BKN);  // wave-uniform
     bf16x2 dsp[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -230,18 +231,32 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(kl + o), qf[ks], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(vl + o), df[ks], dp, 0, 0, 0);
       }
-      // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - LSE2), bf16 pairs
+      // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - LSE2), bf16 pairs;
+      // no per-key test where every row of the wave sees the whole tile
+      if (full) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        float v2[2];
+        for (int q = 0; q < 8; ++q) {
+          float v2[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = 2 * q + u;
-          const bool vis = 32 * kb + acc_row(i, hf) < kv_rel;
-          const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2)) : 0.f;
-          v2[u] = p * (dp[i] - dlt);
+          for (int u = 0; u < 2; ++u) {
+            const int i = 2 * q + u;
+            v2[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2)) * (dp[i] - dlt);
+          }
+          dsp[8 * kb + q] = bf16x2{(__bf16)v2[0], (__bf16)v2[1]};
         }
-        dsp[8 * kb + q] = bf16x2{(__bf16)v2[0], (__bf16)v2[1]};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          float v2[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int i = 2 * q + u;
+            const bool vis = 32 * kb + acc_row(i, hf) < kv_rel;
+            const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2)) : 0.f;
+            v2[u] = p * (dp[i] - dlt);
+          }
+          dsp[8 * kb + q] = bf16x2{(__bf16)v2[0], (__bf16)v2[1]};
+        }
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each half's operands short-lived (register budget)
     }
