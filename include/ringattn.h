@@ -157,8 +157,11 @@ ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l,
  * Tokens on 8GB GPUs in 2026" describes, without padded work).  The arrays
  * k_blocks, v_blocks, kv_pos0, kv_valid are host memory.  Equivalent to
  * init_state, block_fwd for each block in array order (with kv_len =
- * kv_valid[i]), finalize; the fused path keeps the state on chip and may
- * differ from the per-block path only by rounding.
+ * kv_valid[i]), finalize, up to rounding: the fused path keeps the state on
+ * chip, and the per-block path (resident or streamed) processes the first
+ * two blocks that some row can see in four pieces of whole 64-key tiles each,
+ * so that a streamed piece is computed while the next one is copied.  The
+ * two per-block paths give bitwise-equal results.
  *
  * kv_on_host = 0: blocks are device memory.  Unless flags has
  *   RA_FLAG_PERBLOCK, a fused kernel runs (m, l, acc may be NULL when
@@ -166,9 +169,10 @@ ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l,
  * kv_on_host = 1: blocks are pinned host memory (hipHostMalloc'd or
  *   registered), each block densely packed [B, Ck, H, D].  stage_k[0..1] and
  *   stage_v[0..1] are four device slots of B*Ck*H*D elements each; block i is
- *   copied into slot i%2 with hipMemcpyAsync on `copy` while the block before
- *   it is computed on `compute`; per-slot events order the copy before the
- *   kernel and the kernel before the slot's next copy.  m, l, acc are
+ *   copied into slot i%2 (its valid rows, piece by piece) with
+ *   hipMemcpyAsync / hipMemcpy2DAsync on `copy` while the piece or block
+ *   before it is computed on `compute`; events order each piece's copy before
+ *   its kernel and a block's kernels before the slot's next copy.  m, l, acc are
  *   required.  `copy` must differ from `compute`.  The host blocks must stay
  *   alive and unchanged until the compute stream has finished.
  * O and LSE are written on `compute`. */

@@ -113,6 +113,11 @@ ra_status check_mem(const void* p, bool want_host, const char* name) {
 // only ever see these contiguous-equivalent positions.
 int64_t floor_div(int64_t a, int64_t b) { return a / b - ((a % b != 0) && ((a < 0) != (b < 0))); }
 int64_t q_pos_eff(const ra_desc* d) { return d->pos_stride > 1 ? 0 : d->q_pos0; }
+// Pieces per block for the first two blocks of a per-block ring pass.
+#ifndef RA_STREAM_PIECES
+#define RA_STREAM_PIECES 4
+#endif
+
 int64_t kv_pos_eff(const ra_desc* d, int64_t kv_pos0) {
   return d->pos_stride > 1 ? -floor_div(d->q_pos0 - kv_pos0, d->pos_stride) : kv_pos0;
 }
@@ -369,8 +374,6 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
   const bool perblock = kv_on_host || (desc->flags & RA_FLAG_PERBLOCK);
   const bool needs_ws = perblock || (int)live.size() > RA_FUSED_MAX_BLOCKS;
   if (needs_ws && (st = check_state_ptrs(m, l, acc)) != RA_OK) return st;
-  const int64_t block_bytes =
-      (int64_t)desc->batch * desc->kv_len * desc->heads * desc->head_dim * esize(desc->in_dtype);
   if (kv_on_host) {
     if (!stage_k || !stage_v) return fail(RA_E_NULL, "stage_k and stage_v are required when kv_on_host = 1");
     for (int i = 0; i < 2; ++i) {
@@ -435,43 +438,76 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
     return RA_OK;
   }
 
-  // Per-block: init, one launch per live block with the state in HBM, finalize.
+  // Per-block: init, launches with the state in HBM, finalize.  The first
+  // two live blocks go in RA_STREAM_PIECES pieces of whole tiles, the rest
+  // whole: when the blocks stream from host memory, the kernel of a piece
+  // then starts as soon as that piece has landed, and the next piece's copy
+  // runs beside it.  Only the first piece's copy is exposed; it was a whole
+  // block before.  Both per-block paths split the same way, so they stay
+  // bitwise equal.  Pieces that no row can see are skipped.
   e = ra::launch_init_state(rows, desc->head_dim, m, l, acc, compute);
   if (e != hipSuccess) return hip_fail(e, "init_state launch");
+  const int64_t q_last_eff = q_pos_eff(desc) + desc->q_len - 1;
+  auto piece_rows = [&](size_t s, int64_t nv) -> int64_t {
+    if (s >= 2 || RA_STREAM_PIECES <= 1) return nv;
+    const int64_t per = (nv + RA_STREAM_PIECES - 1) / RA_STREAM_PIECES;
+    return (per + 63) / 64 * 64;
+  };
+  auto piece_live = [&](int i, int64_t r0) {
+    return !desc->causal || kv_pos_eff(desc, kv_pos0[i]) + r0 <= q_last_eff;
+  };
+  const int64_t es = esize(desc->in_dtype);
   if (!kv_on_host) {
-    for (int i : live) {
-      t.k[0] = k_blocks[i];
-      t.v[0] = v_blocks[i];
-      t.pos0[0] = kv_pos_eff(desc, kv_pos0[i]);
-      t.len[0] = (int32_t)valid(i);
-      e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
-      if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+    for (size_t s = 0; s < live.size(); ++s) {
+      const int i = live[s];
+      const int64_t nv = valid(i), per = piece_rows(s, nv);
+      for (int64_t r0 = 0; r0 < nv && piece_live(i, r0); r0 += per) {
+        const int64_t off = r0 * desc->kv_stride[1] * es;
+        t.k[0] = (const char*)k_blocks[i] + off;
+        t.v[0] = (const char*)v_blocks[i] + off;
+        t.pos0[0] = kv_pos_eff(desc, kv_pos0[i]) + r0;
+        t.len[0] = (int32_t)(nv - r0 < per ? nv - r0 : per);
+        e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
+        if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+      }
     }
   } else {
     // Two staging slots: block s goes to slot s % 2.  The copy of block s
-    // waits until the kernel of block s-2 (same slot) has finished; the
-    // kernel of block s waits until its copy has landed.
+    // waits until the kernels of block s-2 (same slot) have finished; the
+    // kernel of each piece waits until that piece has landed.  Blocks are
+    // densely packed [B, Ck, H, D]: a piece is a run of rows in each batch.
     if ((e = events_ready()) != hipSuccess) return hip_fail(e, "hipEventCreate");
     if ((e = hipEventRecord(g_ev.start, compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     if ((e = hipStreamWaitEvent(copy, g_ev.start, 0)) != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    const int64_t row_bytes = (int64_t)desc->heads * desc->head_dim * es;
+    const int64_t pitch = desc->kv_len * row_bytes;  // one batch of a block
+    auto copy_rows = [&](void* dst, const void* src, int64_t r0, int64_t r1) -> hipError_t {
+      char* d = (char*)dst + r0 * row_bytes;
+      const char* sp = (const char*)src + r0 * row_bytes;
+      if (desc->batch == 1) return hipMemcpyAsync(d, sp, (size_t)((r1 - r0) * row_bytes), hipMemcpyHostToDevice, copy);
+      return hipMemcpy2DAsync(d, (size_t)pitch, sp, (size_t)pitch, (size_t)((r1 - r0) * row_bytes), (size_t)desc->batch,
+                              hipMemcpyHostToDevice, copy);
+    };
     for (size_t s = 0; s < live.size(); ++s) {
       const int i = live[s];
       const int slot = (int)(s & 1);
       if (s >= 2 && (e = hipStreamWaitEvent(copy, g_ev.free_[slot], 0)) != hipSuccess)
         return hip_fail(e, "hipStreamWaitEvent");
-      if ((e = hipMemcpyAsync(stage_k[slot], k_blocks[i], block_bytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync K");
-      if ((e = hipMemcpyAsync(stage_v[slot], v_blocks[i], block_bytes, hipMemcpyHostToDevice, copy)) != hipSuccess)
-        return hip_fail(e, "hipMemcpyAsync V");
-      if ((e = hipEventRecord(g_ev.full[slot], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-      if ((e = hipStreamWaitEvent(compute, g_ev.full[slot], 0)) != hipSuccess)
-        return hip_fail(e, "hipStreamWaitEvent");
-      t.k[0] = stage_k[slot];
-      t.v[0] = stage_v[slot];
-      t.pos0[0] = kv_pos_eff(desc, kv_pos0[i]);
-      t.len[0] = (int32_t)valid(i);
-      e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
-      if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+      const int64_t nv = valid(i), per = piece_rows(s, nv);
+      for (int64_t r0 = 0; r0 < nv && piece_live(i, r0); r0 += per) {
+        const int64_t r1 = nv - r0 < per ? nv : r0 + per;
+        if ((e = copy_rows(stage_k[slot], k_blocks[i], r0, r1)) != hipSuccess) return hip_fail(e, "hipMemcpyAsync K");
+        if ((e = copy_rows(stage_v[slot], v_blocks[i], r0, r1)) != hipSuccess) return hip_fail(e, "hipMemcpyAsync V");
+        if ((e = hipEventRecord(g_ev.full[slot], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+        if ((e = hipStreamWaitEvent(compute, g_ev.full[slot], 0)) != hipSuccess)
+          return hip_fail(e, "hipStreamWaitEvent");
+        t.k[0] = (const char*)stage_k[slot] + r0 * row_bytes;
+        t.v[0] = (const char*)stage_v[slot] + r0 * row_bytes;
+        t.pos0[0] = kv_pos_eff(desc, kv_pos0[i]) + r0;
+        t.len[0] = (int32_t)(r1 - r0);
+        e = launch_attn(desc, a, t, 1, ra::kLoadStore, compute);
+        if (e != hipSuccess) return hip_fail(e, "block kernel launch");
+      }
       if ((e = hipEventRecord(g_ev.free_[slot], compute)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     }
   }
