@@ -457,6 +457,8 @@ def main():
         "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "pct_of_probed_peak": (100.0 * value / probed) if probed else None,
         "kernel_ms": kern_ms,
+        "kernel_ms_median": sorted(ev_ms)[len(ev_ms) // 2],
+        "kernel_ms_min": min(ev_ms),
         "roofline": roofline,
         "outputs_finite": finite,
     }
