@@ -35,9 +35,16 @@ FLAGS = [
 ]
 
 
+# Per-source flags: the forward kernel and the feedforward GEMM are scheduled
+# with LLVM's iterative ILP strategy (measured 1.2% and 1.9% faster; the
+# backward kernels measured 10% slower with it and keep the default).
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+SOURCE_FLAGS = {"attn_bf16.hip": _ILP, "ffn_bf16.hip": _ILP}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + FLAGS + SOURCE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -480,7 +480,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
       float rs = softmax_exp(sc, c2s, mref, pc);
       __builtin_amdgcn_iglp_opt(3);
       __builtin_amdgcn_sched_barrier(0);
-      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) rs = softmax_redo<C::DB>(sc, c2s, m2, lpart, acc, pc);
+      if (__any(!(rs <= kPLim) || m2 == -INFINITY)) {
+        // (the packed P of the common path is consumed here so that the
+        // compiler forms it inside the interleaved region above instead of
+        // sinking the conversions past this rare branch, which kept 32 fp32
+        // values live and put 16 conversions before the barrier)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) asm volatile("" ::"v"(pc[q]));
+        rs = softmax_redo<C::DB>(sc, c2s, m2, lpart, acc, pc);
+      }
       lpart += rs;
       // slot t+2 (read by tile t+1) has landed; kBufs-2 newer slots may fly
       wait_vm<(kBufs - 2) * 2 * DPW>();
