@@ -78,10 +78,13 @@ def flops(wl) -> int:
 
 
 def kernel_hash() -> str:
+    """Hash of the fused kernel's sources and its per-source build flags."""
+    from long_context_exact_blockwise_amd.build import SOURCE_FLAGS
     h = hashlib.sha256()
     for path in KERNEL_SRC:
         with open(path, "rb") as f:
             h.update(f.read())
+    h.update(repr(SOURCE_FLAGS.get("attn_bf16.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
