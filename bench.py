@@ -432,11 +432,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    traffic = read_traffic() if not perblock else None
+    # the committed counter summary covers the fused kernel on the default workload only
+    traffic = read_traffic() if (not perblock and args.workload == 3) else None
+    kname = "attn_bf16_kernel" if wl.dtype == "bf16" else "attn_f32_kernel"
     roofline = {
         "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
-        "kernel": "attn_bf16_kernel (fused ring pass)" if not perblock else "attn_bf16_kernel (per block)",
+        "kernel": kname + (" (fused ring pass)" if not perblock else " (per block)"),
         "launches_per_step": 1 if (not perblock and len(kb) <= ra.RA_FUSED_MAX_BLOCKS) else None,
         "algorithmic_flop_per_step": f,
         "probed_peak": probed,
