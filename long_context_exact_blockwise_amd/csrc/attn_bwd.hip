@@ -34,6 +34,12 @@
 #include "attn_common.h"
 #include "ra_internal.h"
 
+// The two kernels can be built as separate objects (RA_BWD_PART 1: dq, 2:
+// dK/dV) so that each gets its own scheduling flags; 0 builds both.
+#ifndef RA_BWD_PART
+#define RA_BWD_PART 0
+#endif
+
 namespace ra {
 namespace {
 
@@ -125,6 +131,7 @@ __device__ __forceinline__ bf16x8 pack8(const bf16x2 (&x)[8], int q0) {
 // Clamp a 64-bit tile-relative bound into [lo, hi] as int.
 __device__ __forceinline__ int clamp_i(int64_t x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : (int)x); }
 
+#if RA_BWD_PART != 2
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per BQ query rows of one (b, h); this lane's row r.
 template <int D>
@@ -291,6 +298,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
     }
 }
 
+#endif  // RA_BWD_PART != 2
+
 // ---------------------------------------------------------------------------
 // dK and dV in one pass, split over wave pairs: a workgroup owns 128 keys;
 // wave w (0-3, the P side) and wave w+4 (the dS side) share a SIMD and the
@@ -322,6 +331,7 @@ struct PairStage {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+#if RA_BWD_PART != 1
 template <int D>
 __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<D>;
@@ -525,36 +535,63 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
     }
 }
 
+#endif  // RA_BWD_PART != 1
+
+#if RA_BWD_PART != 2
 template <int D>
-hipError_t launch_d(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_dq(const BwdArgs& a, hipStream_t s) {
   using C = BCfg<D>;
   static bool attr_done = false;  // set once per instantiation; the attribute is idempotent
   if (!attr_done) {
     hipError_t e =
         hipFuncSetAttribute((const void*)bwd_dq_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, C::DQ_LDS);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            PairStage<D>::LDS);
-    if (e != hipSuccess) return e;
     attr_done = true;
   }
   const int64_t nq = (int64_t)a.batch * a.heads * ((a.q_len + BQ - 1) / BQ);
-  const int64_t nk = (int64_t)a.batch * a.heads * ((a.kv_len + BKP - 1) / BKP);
-  if (nq > 0) {
+  if (nq > 0)
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(((nq + 7) / 8) * 8)), dim3(kBThreads), C::DQ_LDS, s, a);
-    hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+#endif
+
+#if RA_BWD_PART != 1
+template <int D>
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
+  static bool attr_done = false;  // set once per instantiation; the attribute is idempotent
+  if (!attr_done) {
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       PairStage<D>::LDS);
     if (e != hipSuccess) return e;
+    attr_done = true;
   }
+  const int64_t nk = (int64_t)a.batch * a.heads * ((a.kv_len + BKP - 1) / BKP);
   if (nk > 0)
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(((nk + 7) / 8) * 8)), dim3(kBThreads), PairStage<D>::LDS,
                        s, a);
   return hipGetLastError();
 }
+#endif
 
 }  // namespace
 
-hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s) {
-  return a.head_dim == 128 ? launch_d<128>(a, s) : launch_d<64>(a, s);
+#if RA_BWD_PART != 2
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? launch_dq<128>(a, s) : launch_dq<64>(a, s);
 }
+#endif
+
+#if RA_BWD_PART != 1
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s) {
+  return a.head_dim == 128 ? launch_dkdv<128>(a, s) : launch_dkdv<64>(a, s);
+}
+#endif
+
+#if RA_BWD_PART != 2
+hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s) {
+  hipError_t e = launch_bwd_dq(a, s);
+  return e != hipSuccess ? e : launch_bwd_dkdv(a, s);
+}
+#endif
 
 }  // namespace ra

@@ -89,7 +89,9 @@ hipError_t launch_finalize(const AttnArgs& a, hipStream_t s);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 // delta[b, h, r] = sum_d dout[b, r, h, d] * o[b, r, h, d]
 hipError_t launch_bwd_delta(const AttnArgs& a, const void* dout, float* delta, hipStream_t s);
-hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_block(const BwdArgs& a, hipStream_t s);  // launch_bwd_dq, then launch_bwd_dkdv
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_fill(float* p, int64_t n, hipStream_t s);
 hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t s);
 hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t s);
