@@ -114,7 +114,9 @@ typedef struct ra_desc {
 #define RA_FUSED_MAX_BLOCKS 64
 
 int ringattn_abi_version(void);
-const char* ringattn_status_str(int status);
+/* Fixed text naming a status (never NULL; "unknown status" for values outside
+ * ra_status). */
+const char* ringattn_status_str(ra_status status);
 /* Detail of the last failing call on this thread ("" if none). */
 const char* ringattn_last_error(void);
 
@@ -132,19 +134,39 @@ ra_status ringattn_ring_order(int32_t q_idx, int32_t num_devices, int32_t* order
  * or a negative pos_stride. */
 int32_t ringattn_block_class(const ra_desc* desc, int64_t kv_pos0);
 
-/* Start a ring pass: m = -inf, l = 0, acc = 0 (device pointers, layouts above). */
+/* Start a ring pass: m = -inf, l = 0, acc = 0, the empty state of the triple
+ * (running max, running sum, unnormalised output) that "Ring Attention: Train
+ * 1M Tokens on 8GB GPUs in 2026", section "Gotchas and Failure Modes", says
+ * each device must carry across chunks.  m, l [B, H, Sq] and acc [B, H, Sq, D]
+ * are fp32 device memory owned by the caller (layouts above); all three are
+ * overwritten.  Errors: RA_E_NULL / RA_E_ALIGN for a missing or misaligned
+ * pointer, RA_E_MEMTYPE if one is not device memory, RA_E_HIP if the launch
+ * fails; nothing is written then. */
 ra_status ringattn_init_state(const ra_desc* desc, float* m, float* l, float* acc, hipStream_t stream);
 
-/* Attend the query chunk q to one KV block (device pointers k, v whose kv_len
- * keys sit at kv_pos0 + j*pos_stride) and fold the result into (m, l, acc) by
- * the online-softmax rule.  A block with fewer valid keys is passed with
- * kv_len set to that count.  A block with no key visible to any row enqueues
- * nothing and returns RA_OK. */
+/* One step of the ring ("Ring Attention: Train 1M Tokens on 8GB GPUs in
+ * 2026", section "Ring Attention: Partition Sequence Length, Not Batch":
+ * each device attends its query chunk to the block it holds at that step):
+ * attend q to one KV block (device pointers k, v whose kv_len keys sit at
+ * kv_pos0 + j*pos_stride) and fold the result into (m, l, acc) by the
+ * online-softmax rule, which keeps the triple of section "Gotchas and
+ * Failure Modes" of the same page exact across chunks whose maxima differ.
+ * q, k, v are read only; m, l, acc are read and rewritten in place (caller
+ * owned, the state of the previous steps).  A block with fewer valid keys is
+ * passed with kv_len set to that count.  A block with no key visible to any
+ * row enqueues nothing and returns RA_OK.  Errors as for init_state, plus
+ * RA_E_SHAPE / RA_E_DTYPE / RA_E_UNSUPPORTED for a descriptor outside the
+ * contract; the state is untouched then. */
 ra_status ringattn_block_fwd(const ra_desc* desc, const void* q, const void* k, const void* v, int64_t kv_pos0,
                              float* m, float* l, float* acc, hipStream_t stream);
 
-/* End a ring pass: O = acc / l in out_dtype (0 where l = 0), LSE = m + ln l
- * (-inf where l = 0). */
+/* End a ring pass: O = acc / l in out_dtype (0 where l = 0), the
+ * softmax(Q K^T * scale) V of the equation in section "Why Standard Attention
+ * Explodes Past 100K Tokens" of "Ring Attention: Train 1M Tokens on 8GB GPUs
+ * in 2026" over every key the state has seen, and LSE = m + ln l (-inf where
+ * l = 0; the log-sum-exp is not on the pages: natural log, fp32 [B, H, Sq]).
+ * m, l, acc are read only; o (desc->out_dtype, o_stride) and lse are written.
+ * Errors as for init_state. */
 ra_status ringattn_finalize(const ra_desc* desc, const float* m, const float* l, const float* acc, void* o,
                             float* lse, hipStream_t stream);
 

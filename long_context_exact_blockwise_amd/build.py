@@ -4,6 +4,12 @@ Every source is compiled with hipcc for gfx950 only; packed-FP32 instructions
 are disabled for all device code (-Xclang -target-feature -Xclang
 -packed-fp32-ops).  Objects go to _build/ next to this file; the shared
 library is written next to this file, where the binding loads it.
+
+A second library, libringattn_check.so, is the same code with the host layer
+built with RA_POISON_STAGING: the host-streamed ring pass fills each staging
+slot with NaN on the copy stream before every copy into it.  Only the tests
+load it (a race between a slot's copy and the kernels that read it then
+shows as NaN or as a difference from the device-resident pass).
 """
 
 from __future__ import annotations
@@ -17,6 +23,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libringattn.so")
+CHECK_OUT = os.path.join(HERE, "libringattn_check.so")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["ringattn_api.hip", "attn_bf16.hip", "attn_bwd.hip", "attn_f32.hip", "ffn_bf16.hip", "probe.hip", "state.hip"]
 
@@ -43,7 +50,10 @@ FLAGS = [
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 SOURCE_FLAGS = {"attn_bf16.hip": _ILP, "ffn_bf16.hip": _ILP}
 # (source, object, extra flags) for sources built more than once
-SPLIT = {"attn_bwd.hip": [("attn_bwd_dq", ["-DRA_BWD_PART=1"]), ("attn_bwd_dkdv", ["-DRA_BWD_PART=2"] + _ILP)]}
+SPLIT = {"attn_bwd.hip": [("attn_bwd_dq", ["-DRA_BWD_PART=1"]), ("attn_bwd_dkdv", ["-DRA_BWD_PART=2"] + _ILP)],
+         "ringattn_api.hip": [("ringattn_api", []), ("ringattn_api_check", ["-DRA_POISON_STAGING=1"])]}
+CHECK_ONLY = {"ringattn_api_check"}  # objects of the checking library only
+MAIN_ONLY = {"ringattn_api"}         # objects it replaces
 
 
 def _compile_one(src: str, name: str, extra: list) -> str:
@@ -64,19 +74,25 @@ def _jobs():
             yield src, os.path.splitext(src)[0], SOURCE_FLAGS.get(src, [])
 
 
+def _link(out: str, objs: list) -> None:
+    tmp = out + ".tmp"
+    cmd = [hipcc(), "-shared", "--offload-arch=gfx950", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     jobs = list(_jobs())
     with cf.ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
         objs = list(ex.map(lambda j: _compile_one(*j), jobs))
-    tmp = OUT + ".tmp"
-    cmd = [hipcc(), "-shared", "--offload-arch=gfx950", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    names = [j[1] for j in jobs]
+    _link(OUT, [o for o, n in zip(objs, names) if n not in CHECK_ONLY])
+    _link(CHECK_OUT, [o for o, n in zip(objs, names) if n not in MAIN_ONLY])
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {CHECK_OUT}")
     return OUT
 
 

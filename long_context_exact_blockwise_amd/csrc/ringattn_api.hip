@@ -39,6 +39,30 @@ int esize(int32_t dt) { return dt == RA_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// True when the rows of D contiguous elements of a [B, S, H, D] tensor with
+// element strides st[3] along (b, s, h) are pairwise disjoint: taking the
+// dimensions of extent > 1 from the smallest stride up, each stride must
+// reach past everything the inner dimensions already span.
+bool rows_disjoint(const int64_t st[3], int64_t nb, int64_t ns, int64_t nh, int64_t d) {
+  int64_t ext[3] = {nb, ns, nh};
+  int idx[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i)  // sort the three dims by stride
+    for (int j = i + 1; j < 3; ++j)
+      if (st[idx[j]] < st[idx[i]]) {
+        const int t = idx[i];
+        idx[i] = idx[j];
+        idx[j] = t;
+      }
+  int64_t span = d;  // elements [0, span) covered by the inner dims
+  for (int i = 0; i < 3; ++i) {
+    const int k = idx[i];
+    if (ext[k] <= 1) continue;
+    if (st[k] < span) return false;
+    span = st[k] * (ext[k] - 1) + span;
+  }
+  return true;
+}
+
 // Host-only checks of a descriptor (no HIP calls).
 ra_status check_desc(const ra_desc* d) {
   if (!d) return fail(RA_E_NULL, "desc is NULL");
@@ -70,6 +94,10 @@ ra_status check_desc(const ra_desc* d) {
   // Key rows of a block may not overlap (the copies into LDS rely on it).
   if (d->kv_len > 1 && d->kv_stride[1] < d->head_dim)
     return fail(RA_E_SHAPE, "kv_stride[1] (%lld) must be >= head_dim", (long long)d->kv_stride[1]);
+  // O is written: no two (b, s, h) rows of D elements may share an element.
+  if (!rows_disjoint(d->o_stride, d->batch, d->q_len, d->heads, d->head_dim))
+    return fail(RA_E_SHAPE, "o_stride (%lld, %lld, %lld) makes rows of O overlap", (long long)d->o_stride[0],
+                (long long)d->o_stride[1], (long long)d->o_stride[2]);
   // The kernels count keys of a block and tiles with 32-bit integers.
   if (d->kv_len >= ((int64_t)1 << 30))
     return fail(RA_E_UNSUPPORTED, "kv_len (%lld) must be below 2^30", (long long)d->kv_len);
@@ -113,6 +141,15 @@ ra_status check_mem(const void* p, bool want_host, const char* name) {
 // only ever see these contiguous-equivalent positions.
 int64_t floor_div(int64_t a, int64_t b) { return a / b - ((a % b != 0) && ((a < 0) != (b < 0))); }
 int64_t q_pos_eff(const ra_desc* d) { return d->pos_stride > 1 ? 0 : d->q_pos0; }
+// Checking build only (built as a separate library for the tests): before
+// each piece's copy into a staging slot, the slot rows it is about to fill are
+// set to NaN on the copy stream, so a kernel that reads a slot before its
+// copy has landed, or a copy that overwrites a slot still being read, shows
+// up as NaN or as a difference from the device-resident pass.
+#ifndef RA_POISON_STAGING
+#define RA_POISON_STAGING 0
+#endif
+
 // Pieces per block for the first two blocks of a per-block ring pass.
 #ifndef RA_STREAM_PIECES
 #define RA_STREAM_PIECES 4
@@ -257,7 +294,7 @@ extern "C" {
 
 int ringattn_abi_version(void) { return RINGATTN_ABI_VERSION; }
 
-const char* ringattn_status_str(int status) {
+const char* ringattn_status_str(ra_status status) {
   switch (status) {
     case RA_OK: return "RA_OK";
     case RA_E_NULL: return "RA_E_NULL: required pointer is NULL";
@@ -496,6 +533,13 @@ ra_status ringattn_ring_fwd(const ra_desc* desc, const void* q, const void* cons
       const int64_t nv = valid(i), per = piece_rows(s, nv);
       for (int64_t r0 = 0; r0 < nv && piece_live(i, r0); r0 += per) {
         const int64_t r1 = nv - r0 < per ? nv : r0 + per;
+#if RA_POISON_STAGING
+        for (int b = 0; b < desc->batch; ++b)
+          for (void* dst : {stage_k[slot], stage_v[slot]})
+            if ((e = ra::launch_fill_u32((char*)dst + b * pitch + r0 * row_bytes, (r1 - r0) * row_bytes / 4,
+                                         0xFFFFFFFFu, copy)) != hipSuccess)
+              return hip_fail(e, "poison launch");
+#endif
         if ((e = copy_rows(stage_k[slot], k_blocks[i], r0, r1)) != hipSuccess) return hip_fail(e, "hipMemcpyAsync K");
         if ((e = copy_rows(stage_v[slot], v_blocks[i], r0, r1)) != hipSuccess) return hip_fail(e, "hipMemcpyAsync V");
         if ((e = hipEventRecord(g_ev.full[slot], copy)) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -87,9 +87,11 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(AttnArgs a, const _
   if (row < nrow && part == 0) delta[row] = sum;
 }
 
-__global__ __launch_bounds__(kThreads) void fill_zero_kernel(float* p, int64_t n) {
+// n 32-bit words set to `value` (0 is +0.0f; all ones is a NaN both as one
+// fp32 and as two bf16 values).
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t value) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
-    p[i] = 0.f;
+    p[i] = value;
 }
 
 unsigned grid_for(int64_t n) {
@@ -135,9 +137,11 @@ hipError_t launch_bwd_delta(const AttnArgs& a, const void* dout, float* delta, h
   return hipGetLastError();
 }
 
-hipError_t launch_fill(float* p, int64_t n, hipStream_t s) {
+hipError_t launch_fill(float* p, int64_t n, hipStream_t s) { return launch_fill_u32(p, n, 0u, s); }
+
+hipError_t launch_fill_u32(void* p, int64_t n, uint32_t value, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, p, n);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n)), dim3(kThreads), 0, s, (uint32_t*)p, n, value);
   return hipGetLastError();
 }
 

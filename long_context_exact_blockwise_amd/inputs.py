@@ -36,10 +36,11 @@ class Workload:
     in_scale: float = 1.0
     batch: int = 1
     host_streamed: bool = False
+    q_pos_base: Optional[int] = None  # global position of query row 0 when it is not q_idx * q_len
 
     @property
     def q_pos0(self) -> int:
-        return self.q_idx * self.q_len
+        return self.q_idx * self.q_len if self.q_pos_base is None else self.q_pos_base
 
     def kv_pos0(self, j: int) -> int:
         return j * self.kv_len

@@ -64,12 +64,18 @@ _lib = None
 def lib():
     """Load the library once; raise if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+    if _lib is None:
+        _lib = load(LIB_PATH)
+    return _lib
+
+
+def load(path: str):
+    """Open a build of the library at `path` and declare its C signatures
+    (the functions below call the one lib() returns)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                            "(or python -m long_context_exact_blockwise_amd.build)")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P = ctypes.c_void_p
     D = ctypes.POINTER(RaDesc)
     L.ringattn_abi_version.restype = ctypes.c_int
@@ -105,8 +111,7 @@ def lib():
                                     ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P, P, P, P,
                                     ctypes.POINTER(P), ctypes.POINTER(P), P]
     if L.ringattn_abi_version() != ABI_VERSION:
-        raise RuntimeError("libringattn.so ABI version mismatch")
-    _lib = L
+        raise RuntimeError(f"{path}: ABI version mismatch")
     return L
 
 

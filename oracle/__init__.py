@@ -28,7 +28,9 @@ What it computes, and from which passage:
 * ``ring_attention_bwd`` / ``delta`` (``backward.py``): the exact gradients of
   that output with respect to Q, K and V for an upstream dO (the pages train
   through the ring but never write the backward pass; the reading is stated
-  in that module).
+  in that module); ``key_rows_bwd`` gives the same dK and dV for chosen keys
+  only, over all query rows, so that long sequences can be checked key by
+  key.
 * ``blockwise_ffn`` / ``gelu_tanh`` (``ffn.py``): the position-wise
   feedforward computed over row blocks ("Ring Attention with Blockwise
   Transformers for Near-Infinite Context", Abstract: blockwise computation of
@@ -46,5 +48,5 @@ from .attention import (  # noqa: F401
     ring_attention,
     visible,
 )
-from .backward import delta, ring_attention_bwd  # noqa: F401
+from .backward import delta, key_rows_bwd, ring_attention_bwd  # noqa: F401
 from .ffn import blockwise_ffn, gelu_tanh  # noqa: F401

@@ -87,3 +87,67 @@ def delta(o, do):
     o = np.asarray(o, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     return np.transpose((o * do).sum(axis=3), (0, 2, 1))
+
+
+def key_rows_bwd(q, do, k_blocks: Sequence, v_blocks: Sequence, q_pos0: int, kv_pos0s: Sequence[int], causal: bool,
+                 key_rows: Sequence, scale: float | None = None, pos_stride: int = 1, chunk: int = 256):
+    """dK and dV of chosen keys only, summed over every query row of q.
+
+    The same gradient as ``ring_attention_bwd`` (module docstring), kept to
+    the keys that are asked for, so that a long sequence can be checked
+    without forming every key's gradient:
+      dV_c = sum_r P[r, c] dO_r,   dK_c = scale sum_r P[r, c] (dP[r, c] - delta_r) q_r
+    where P[r, :] is the softmax row of query r over ALL visible keys of all
+    blocks, dP[r, c] = <dO_r, v_c> and delta_r = sum_c' P[r, c'] dP[r, c']
+    over all of them too.  Query rows are taken `chunk` at a time (each
+    chunk's full score rows, then its terms for the chosen keys), which
+    bounds the memory; dK_c and dV_c are sums over rows, so the chunking
+    changes nothing but the order of the additions.
+
+    q, do: [B, Sq, H, D]; blocks and positions as in ``ring_attention_bwd``.
+    key_rows: pairs (j, i), key i of block j (block indices as passed).
+    Returns (dK [B, n, H, D], dV [B, n, H, D]) in float64, n = len(key_rows),
+    in the order of key_rows.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    bsz, sq, nh, d = q.shape
+    if scale is None:
+        scale = default_scale(d)
+    kbs = [np.asarray(k, dtype=np.float64) for k in k_blocks]
+    vbs = [np.asarray(v, dtype=np.float64) for v in v_blocks]
+    n = len(key_rows)
+    dv_dim = vbs[0].shape[3] if vbs else d
+    dk = np.zeros((bsz, n, nh, d))
+    dv = np.zeros((bsz, n, nh, dv_dim))
+    if n == 0 or sq == 0:
+        return dk, dv
+    # every key of every block, in the order the blocks are given
+    starts = np.concatenate([[0], np.cumsum([k.shape[1] for k in kbs])]).astype(np.int64)
+    kv_pos = np.concatenate([int(kv_pos0s[j]) + int(pos_stride) * np.arange(kbs[j].shape[1], dtype=np.int64)
+                             for j in range(len(kbs))])
+    sel = np.array([starts[j] + i for j, i in key_rows], dtype=np.int64)
+    q_pos = int(q_pos0) + int(pos_stride) * np.arange(sq, dtype=np.int64)
+    for b in range(bsz):
+        for h in range(nh):
+            kh = np.concatenate([k[b, :, h, :] for k in kbs], axis=0)
+            vh = np.concatenate([v[b, :, h, :] for v in vbs], axis=0)
+            for r0 in range(0, sq, chunk):
+                r1 = min(sq, r0 + chunk)
+                vis = visible(q_pos[r0:r1], kv_pos, causal)
+                has = vis.any(axis=1)
+                if not has.any():
+                    continue
+                qc = q[b, r0:r1, h, :][has]
+                doc = do[b, r0:r1, h, :][has]
+                s = np.where(vis[has], scale * (qc @ kh.T), -np.inf)
+                m = s.max(axis=1, keepdims=True)
+                e = np.exp(s - m)
+                p = e / e.sum(axis=1, keepdims=True)
+                dp = doc @ vh.T
+                delta_r = (p * dp).sum(axis=1, keepdims=True)
+                p_sel = p[:, sel]
+                ds_sel = p_sel * (dp[:, sel] - delta_r)
+                dk[b, :, h, :] += scale * (ds_sel.T @ qc)
+                dv[b, :, h, :] += p_sel.T @ doc
+    return dk, dv

@@ -108,4 +108,42 @@ def pin_bwd_delta(bwd, fwd):
         assert np.allclose((p * (do[0, :, h] @ vh.T)).sum(axis=1), d[0, h], rtol=0, atol=1e-12)
 
 
-ALL_BWD_PINS = [pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants, pin_bwd_delta]
+def _autograd_grads(q, kb, vb, q0, pos, causal, do, pos_stride=1):
+    """dK, dV of every block from torch autograd (fp64) of a plain masked
+    softmax attention over the concatenated keys."""
+    qt = torch.tensor(q)
+    kts = [torch.tensor(k, requires_grad=True) for k in kb]
+    vts = [torch.tensor(v, requires_grad=True) for v in vb]
+    kpos = torch.cat([p + pos_stride * torch.arange(k.shape[1]) for p, k in zip(pos, kb)])
+    qpos = q0 + pos_stride * torch.arange(q.shape[1])
+    mask = (kpos[None, :] <= qpos[:, None]) if causal else torch.ones((q.shape[1], kpos.shape[0]), dtype=torch.bool)
+    s = torch.einsum("bqhd,bkhd->bhqk", qt, torch.cat(kts, dim=1)) / np.sqrt(q.shape[3])
+    s = s.masked_fill(~mask, float("-inf"))
+    p = torch.nan_to_num(torch.softmax(s, dim=-1))  # rows without a visible key: no weight
+    o = torch.einsum("bhqk,bkhd->bqhd", p, torch.cat(vts, dim=1))
+    (o * torch.tensor(do)).sum().backward()
+    return [t.grad.numpy() for t in kts], [t.grad.numpy() for t in vts]
+
+
+def pin_bwd_key_rows(bwd, fwd):
+    """The chosen-keys gradient equals the gradient of those keys from torch
+    autograd and from the whole-tensor oracle, whatever the row chunking:
+    blocks out of position order, keys asked for in a scrambled order with
+    repeats, causal and not, striped positions, and query rows that see no
+    key at all."""
+    q, kb, vb, q0, pos, _, do = _case(11)
+    picks = [(2, 3), (0, 0), (1, 1), (2, 0), (0, 2), (1, 0), (2, 3), (0, 1), (2, 1), (2, 2)]
+    for causal, q0_, ps in ((True, q0, 1), (False, q0, 1), (True, 1, 1), (True, 2, 3), (True, -5, 1)):
+        gk, gv = _autograd_grads(q, kb, vb, q0_, pos, causal, do, pos_stride=ps)
+        _, fk, fv = bwd.ring_attention_bwd(q, kb, vb, q0_, pos, causal, do, pos_stride=ps)
+        for chunk in (1, 3, 256):
+            dk, dv = bwd.key_rows_bwd(q, do, kb, vb, q0_, pos, causal, picks, pos_stride=ps, chunk=chunk)
+            for n, (j, i) in enumerate(picks):
+                assert np.allclose(dk[:, n], gk[j][:, i], rtol=0, atol=1e-12), (causal, q0_, ps, chunk, j, i)
+                assert np.allclose(dv[:, n], gv[j][:, i], rtol=0, atol=1e-12), (causal, q0_, ps, chunk, j, i)
+                assert np.allclose(dk[:, n], fk[j][:, i], rtol=0, atol=1e-12)
+                assert np.allclose(dv[:, n], fv[j][:, i], rtol=0, atol=1e-12)
+
+
+ALL_BWD_PINS = [pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants, pin_bwd_delta,
+                pin_bwd_key_rows]

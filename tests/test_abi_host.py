@@ -120,11 +120,22 @@ def _ring(d, q=FAKE, o=FAKE, lse=FAKE, kb=(FAKE,), vb=(FAKE,), pos=(0,), on_host
     (dict(kv_stride=(256 * 256, 64, 128)), ra.RA_E_SHAPE),   # key rows overlap (stride < head_dim)
     (dict(flags=4), ra.RA_E_UNSUPPORTED),
     (dict(pos_stride=-1), ra.RA_E_SHAPE),
+    (dict(o_stride=(256 * 256, 256, 64)), ra.RA_E_SHAPE),            # the two heads of a row of O overlap
+    (dict(heads=1, o_stride=(256 * 128, 64, 128)), ra.RA_E_SHAPE),   # consecutive rows of O overlap
+    (dict(batch=2, o_stride=(1000, 256, 128)), ra.RA_E_SHAPE),       # batch 1 starts inside batch 0
 ])
 def test_descriptor_rejected_before_enqueue(kw, status):
     st, msg = _ring(_desc(**kw))
     assert st == status, (st, msg)
     assert msg
+
+
+@pytest.mark.parametrize("o_stride", [(2 * 256 * 128, 128, 256 * 128),   # [B, H, S, D]: heads outer
+                                      (256 * 256, 256, 128),             # the default [B, S, H, D]
+                                      (256 * 512, 512, 256)])            # padded rows
+def test_disjoint_output_layouts_pass_the_overlap_check(o_stride):
+    st, msg = _ring(_desc(o_stride=o_stride))
+    assert st != ra.RA_E_SHAPE, msg
 
 
 def test_pointer_checks_before_enqueue():

@@ -33,3 +33,10 @@ def test_forward_flags_in_traffic_hash(monkeypatch):
     h0 = bench.kernel_hash()
     monkeypatch.setitem(build.SOURCE_FLAGS, "attn_bf16.hip", [])
     assert bench.kernel_hash() != h0
+
+
+def test_checking_library_differs_only_in_the_host_layer():
+    jobs = {n: (s, f) for s, n, f in build._jobs()}
+    assert jobs["ringattn_api_check"] == ("ringattn_api.hip", ["-DRA_POISON_STAGING=1"])
+    assert jobs["ringattn_api"] == ("ringattn_api.hip", [])
+    assert build.CHECK_ONLY == {"ringattn_api_check"} and build.MAIN_ONLY == {"ringattn_api"}

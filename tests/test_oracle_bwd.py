@@ -34,6 +34,16 @@ MUTANTS = {
     "mask_ignored": ("s = np.where(vis, scale * (qh @ kh.T), -np.inf)", "s = scale * (qh @ kh.T)"),
     "dv_from_ds": ("dvh = p.T @ doh", "dvh = ds.T @ doh"),
     "blocks_in_given_order": ("for pos, j in enumerate(order):", "for pos, j in enumerate(range(nblk)):"),
+    # the chosen-keys gradient (key_rows_bwd)
+    "key_rows_delta_over_chosen": ("delta_r = (p * dp).sum(axis=1, keepdims=True)",
+                                   "delta_r = (p[:, sel] * dp[:, sel]).sum(axis=1, keepdims=True)"),
+    "key_rows_normaliser_over_chosen": ("p = e / e.sum(axis=1, keepdims=True)",
+                                        "p = e / e[:, sel].sum(axis=1, keepdims=True)"),
+    "key_rows_chunk_positions": ("vis = visible(q_pos[r0:r1], kv_pos, causal)",
+                                 "vis = visible(q_pos[:r1 - r0], kv_pos, causal)"),
+    "key_rows_block_offset": ("sel = np.array([starts[j] + i for j, i in key_rows]",
+                              "sel = np.array([i for j, i in key_rows]"),
+    "key_rows_dk_no_scale": ("dk[b, :, h, :] += scale * (ds_sel.T @ qc)", "dk[b, :, h, :] += ds_sel.T @ qc"),
 }
 
 
