@@ -54,7 +54,8 @@
  * valid once the compute stream has finished.  Faults inside kernels surface
  * at the caller's next synchronisation.  Nothing throws or aborts across the
  * ABI.  Calls that share buffers on overlapping streams race; calls on
- * disjoint buffers may run concurrently.
+ * disjoint buffers may run concurrently (ringattn_ring_bwd_noalloc excepted:
+ * its calls share one device array per GPU).
  */
 #ifndef RINGATTN_H
 #define RINGATTN_H
@@ -235,6 +236,22 @@ ra_status ringattn_ring_bwd(const ra_desc* desc, const void* q, const void* cons
                             const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
                             int32_t num_blocks, const void* o, const void* dout, const float* lse, float* delta,
                             float* dq, float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream);
+
+/* ringattn_ring_bwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and arguments without the delta
+ * workspace.  Its [B, H, Sq] fp32 delta lives in a file-scope device array of
+ * RINGATTN_NOALLOC_MAX_ROWS floats (16 MiB) that the library holds on each GPU
+ * it runs on until the process ends; the call itself makes no allocation.
+ * batch * heads * q_len above RINGATTN_NOALLOC_MAX_ROWS gives
+ * RA_E_UNSUPPORTED before anything is enqueued.  All calls on one GPU share
+ * that array (each call overwrites it before reading it): calls that overlap
+ * on one GPU, on any streams, race. */
+#define RINGATTN_NOALLOC_MAX_ROWS (4 << 20)
+ra_status ringattn_ring_bwd_noalloc(const ra_desc* desc, const void* q, const void* const* k_blocks,
+                                    const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
+                                    int32_t num_blocks, const void* o, const void* dout, const float* lse, float* dq,
+                                    float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream);
 
 /* ---- Blockwise feedforward ("Ring Attention with Blockwise Transformers for
  * Near-Infinite Context", Abstract: blockwise computation of self-attention

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -257,6 +258,35 @@ ra_status check_bwd_desc(const ra_desc* d) {
   return RA_OK;
 }
 
+// ---- the scratch of ringattn_ring_bwd_noalloc ----
+// Its per-row delta lives in this file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends).  In host code
+// the name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns, taken once per device with that device current
+// and kept in g_scratch.  Every call on one GPU shares the array; calls that
+// overlap on one GPU race.
+static __device__ __align__(256) float scratch[RINGATTN_NOALLOC_MAX_ROWS];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch[kMaxDevices] = {};
+
+ra_status scratch_address(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RA_E_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess)
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = (float*)p;
+  }
+  *out = g_scratch[dev];
+  return RA_OK;
+}
+
 BwdArgs make_bwd(const ra_desc* d, const void* q, const void* k, const void* v, int64_t kv_pos0, int64_t valid,
                  const void* dout, const float* lse, const float* delta, float* dq, float* dk, float* dv) {
   BwdArgs a;
@@ -288,6 +318,60 @@ BwdArgs make_bwd(const ra_desc* d, const void* q, const void* k, const void* v, 
   a.scale = d->scale > 0.f ? d->scale : (float)(1.0 / std::sqrt((double)d->head_dim));
   return a;
 }
+// The ring backward; delta is the caller's workspace, or (use_scratch) the
+// library's per-device scratch array.
+ra_status ring_bwd(const ra_desc* desc, const void* q, const void* const* k_blocks, const void* const* v_blocks,
+                   const int64_t* kv_pos0, const int64_t* kv_valid, int32_t num_blocks, const void* o,
+                   const void* dout, const float* lse, float* delta, bool use_scratch, float* dq,
+                   float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream) {
+  ra_status st;
+  if ((st = check_bwd_desc(desc)) != RA_OK) return st;
+  if (num_blocks < 0) return fail(RA_E_SHAPE, "num_blocks must be >= 0");
+  if (use_scratch && (int64_t)desc->batch * desc->heads * desc->q_len > RINGATTN_NOALLOC_MAX_ROWS)
+    return fail(RA_E_UNSUPPORTED, "batch * heads * q_len = %lld exceeds the %d rows of the scratch delta",
+                (long long)desc->batch * desc->heads * desc->q_len, RINGATTN_NOALLOC_MAX_ROWS);
+  if (desc->q_len == 0) return RA_OK;
+  if (num_blocks > 0 && (!k_blocks || !v_blocks || !kv_pos0 || !dk_blocks || !dv_blocks))
+    return fail(RA_E_NULL, "k_blocks, v_blocks, kv_pos0, dk_blocks and dv_blocks are required when num_blocks > 0");
+  const void* ptrs[] = {q, o, dout, lse, dq, delta};
+  const char* names[] = {"q", "o", "dout", "lse", "dq", "delta"};
+  const int nptr = use_scratch ? 5 : 6;  // the scratch delta is the library's own
+  for (int i = 0; i < nptr; ++i)
+    if ((st = need_ptr(ptrs[i], names[i])) != RA_OK) return st;
+  auto valid = [&](int i) -> int64_t { return kv_valid ? kv_valid[i] : desc->kv_len; };
+  for (int i = 0; i < num_blocks; ++i) {
+    if ((st = need_ptr(k_blocks[i], "k_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(v_blocks[i], "v_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(dk_blocks[i], "dk_blocks[i]")) != RA_OK) return st;
+    if ((st = need_ptr(dv_blocks[i], "dv_blocks[i]")) != RA_OK) return st;
+    if (valid(i) < 0 || valid(i) > desc->kv_len)
+      return fail(RA_E_SHAPE, "kv_valid[%d] = %lld must be in [0, kv_len = %lld]", i, (long long)valid(i),
+                  (long long)desc->kv_len);
+  }
+  for (int i = 0; i < nptr; ++i)
+    if ((st = check_mem(ptrs[i], false, names[i])) != RA_OK) return st;
+  for (int i = 0; i < num_blocks; ++i) {
+    if ((st = check_mem(k_blocks[i], false, "k_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(v_blocks[i], false, "v_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(dk_blocks[i], false, "dk_blocks[i]")) != RA_OK) return st;
+    if ((st = check_mem(dv_blocks[i], false, "dv_blocks[i]")) != RA_OK) return st;
+  }
+  if (use_scratch && (st = scratch_address(&delta)) != RA_OK) return st;
+  AttnArgs da = make_args(desc, nullptr, (void*)o, nullptr, nullptr, nullptr, nullptr);
+  hipError_t e = ra::launch_bwd_delta(da, dout, delta, stream);
+  if (e != hipSuccess) return hip_fail(e, "delta launch");
+  e = ra::launch_fill(dq, (int64_t)desc->batch * desc->q_len * desc->heads * desc->head_dim, stream);
+  if (e != hipSuccess) return hip_fail(e, "fill launch");
+  for (int i = 0; i < num_blocks; ++i) {
+    if (classify(desc, kv_pos0[i], valid(i)) == RA_BLOCK_SKIP) continue;
+    BwdArgs a = make_bwd(desc, q, k_blocks[i], v_blocks[i], kv_pos0[i], valid(i), dout, lse, delta, dq,
+                         dk_blocks[i], dv_blocks[i]);
+    e = ra::launch_bwd_block(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward block launch");
+  }
+  return RA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -600,47 +684,17 @@ ra_status ringattn_ring_bwd(const ra_desc* desc, const void* q, const void* cons
                             int32_t num_blocks, const void* o, const void* dout, const float* lse, float* delta,
                             float* dq, float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream) {
   g_err.clear();
-  ra_status st;
-  if ((st = check_bwd_desc(desc)) != RA_OK) return st;
-  if (num_blocks < 0) return fail(RA_E_SHAPE, "num_blocks must be >= 0");
-  if (desc->q_len == 0) return RA_OK;
-  if (num_blocks > 0 && (!k_blocks || !v_blocks || !kv_pos0 || !dk_blocks || !dv_blocks))
-    return fail(RA_E_NULL, "k_blocks, v_blocks, kv_pos0, dk_blocks and dv_blocks are required when num_blocks > 0");
-  const void* ptrs[] = {q, o, dout, lse, delta, dq};
-  const char* names[] = {"q", "o", "dout", "lse", "delta", "dq"};
-  for (int i = 0; i < 6; ++i)
-    if ((st = need_ptr(ptrs[i], names[i])) != RA_OK) return st;
-  auto valid = [&](int i) -> int64_t { return kv_valid ? kv_valid[i] : desc->kv_len; };
-  for (int i = 0; i < num_blocks; ++i) {
-    if ((st = need_ptr(k_blocks[i], "k_blocks[i]")) != RA_OK) return st;
-    if ((st = need_ptr(v_blocks[i], "v_blocks[i]")) != RA_OK) return st;
-    if ((st = need_ptr(dk_blocks[i], "dk_blocks[i]")) != RA_OK) return st;
-    if ((st = need_ptr(dv_blocks[i], "dv_blocks[i]")) != RA_OK) return st;
-    if (valid(i) < 0 || valid(i) > desc->kv_len)
-      return fail(RA_E_SHAPE, "kv_valid[%d] = %lld must be in [0, kv_len = %lld]", i, (long long)valid(i),
-                  (long long)desc->kv_len);
-  }
-  for (int i = 0; i < 6; ++i)
-    if ((st = check_mem(ptrs[i], false, names[i])) != RA_OK) return st;
-  for (int i = 0; i < num_blocks; ++i) {
-    if ((st = check_mem(k_blocks[i], false, "k_blocks[i]")) != RA_OK) return st;
-    if ((st = check_mem(v_blocks[i], false, "v_blocks[i]")) != RA_OK) return st;
-    if ((st = check_mem(dk_blocks[i], false, "dk_blocks[i]")) != RA_OK) return st;
-    if ((st = check_mem(dv_blocks[i], false, "dv_blocks[i]")) != RA_OK) return st;
-  }
-  AttnArgs da = make_args(desc, nullptr, (void*)o, nullptr, nullptr, nullptr, nullptr);
-  hipError_t e = ra::launch_bwd_delta(da, dout, delta, stream);
-  if (e != hipSuccess) return hip_fail(e, "delta launch");
-  e = ra::launch_fill(dq, (int64_t)desc->batch * desc->q_len * desc->heads * desc->head_dim, stream);
-  if (e != hipSuccess) return hip_fail(e, "fill launch");
-  for (int i = 0; i < num_blocks; ++i) {
-    if (classify(desc, kv_pos0[i], valid(i)) == RA_BLOCK_SKIP) continue;
-    BwdArgs a = make_bwd(desc, q, k_blocks[i], v_blocks[i], kv_pos0[i], valid(i), dout, lse, delta, dq,
-                         dk_blocks[i], dv_blocks[i]);
-    e = ra::launch_bwd_block(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "backward block launch");
-  }
-  return RA_OK;
+  return ring_bwd(desc, q, k_blocks, v_blocks, kv_pos0, kv_valid, num_blocks, o, dout, lse, delta, false, dq, dk_blocks,
+                  dv_blocks, stream);
+}
+
+ra_status ringattn_ring_bwd_noalloc(const ra_desc* desc, const void* q, const void* const* k_blocks,
+                                    const void* const* v_blocks, const int64_t* kv_pos0, const int64_t* kv_valid,
+                                    int32_t num_blocks, const void* o, const void* dout, const float* lse, float* dq,
+                                    float* const* dk_blocks, float* const* dv_blocks, hipStream_t stream) {
+  g_err.clear();
+  return ring_bwd(desc, q, k_blocks, v_blocks, kv_pos0, kv_valid, num_blocks, o, dout, lse, nullptr, true, dq,
+                  dk_blocks, dv_blocks, stream);
 }
 
 ra_status ringattn_ffn_fwd(const ra_ffn_desc* d, const void* x, const void* w1, const void* b1, const void* w2,

@@ -30,8 +30,9 @@ SYMBOLS = (
     "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
     "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
     "ringattn_ring_fwd", "ringattn_probe_copy", "ringattn_bwd_delta", "ringattn_block_bwd", "ringattn_ring_bwd",
-    "ringattn_ffn_fwd", "ringattn_probe_mfma",
+    "ringattn_ffn_fwd", "ringattn_probe_mfma", "ringattn_ring_bwd_noalloc",
 )
+NOALLOC_MAX_ROWS = 4 << 20
 
 
 class RingAttnError(RuntimeError):
@@ -110,6 +111,10 @@ def load(path: str):
     L.ringattn_ring_bwd.argtypes = [D, P, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(ctypes.c_int64),
                                     ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, P, P, P, P, P,
                                     ctypes.POINTER(P), ctypes.POINTER(P), P]
+    L.ringattn_ring_bwd_noalloc.restype = ctypes.c_int
+    L.ringattn_ring_bwd_noalloc.argtypes = [D, P, ctypes.POINTER(P), ctypes.POINTER(P),
+                                            ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                            ctypes.c_int32, P, P, P, P, ctypes.POINTER(P), ctypes.POINTER(P), P]
     if L.ringattn_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path}: ABI version mismatch")
     return L
@@ -285,6 +290,19 @@ def ringattn_ring_bwd(desc: RaDesc, q, k_blocks: Sequence, v_blocks: Sequence, k
     _check(lib().ringattn_ring_bwd(ctypes.byref(desc), _ptr(q), arr(k_blocks), arr(v_blocks), pp, nv, n, _ptr(o),
                                    _ptr(dout), _ptr(lse), _ptr(delta), _ptr(dq), arr(dk_blocks), arr(dv_blocks),
                                    _stream(stream)))
+
+
+def ringattn_ring_bwd_noalloc(desc: RaDesc, q, k_blocks: Sequence, v_blocks: Sequence, kv_pos0: Sequence[int], o,
+                              dout, lse, dq, dk_blocks: Sequence, dv_blocks: Sequence, *,
+                              kv_valid: Optional[Sequence[int]] = None, stream=None):
+    n = len(k_blocks)
+    P = ctypes.c_void_p
+    arr = lambda ts: (P * max(n, 1))(*[t.data_ptr() for t in ts])  # noqa: E731
+    pp = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_pos0])
+    nv = None if kv_valid is None else (ctypes.c_int64 * max(n, 1))(*[int(x) for x in kv_valid])
+    _check(lib().ringattn_ring_bwd_noalloc(ctypes.byref(desc), _ptr(q), arr(k_blocks), arr(v_blocks), pp, nv, n,
+                                           _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), arr(dk_blocks), arr(dv_blocks),
+                                           _stream(stream)))
 
 
 def ring_backward(q: torch.Tensor, k_blocks: Sequence[torch.Tensor], v_blocks: Sequence[torch.Tensor],
