@@ -17,7 +17,15 @@ sums of dK and dV over all keys checked against their closed forms.
 Unless --no-ffn, it also carries `ffn`: the blockwise feedforward of the
 1.3B model's layer (d 2048, d_ff 8192, tanh GELU) over the same 128K-row
 chunk in 16K-row blocks, in TFLOP/s of its two products (4*rows*d*d_ff),
-with sampled rows checked against the oracle.
+with sampled rows checked against the oracle, and beside it torch's own path
+for the same blockwise network (hipBLASLt GEMMs with bias, then GELU) as a
+stated baseline.
+
+Unless --no-workloads (default workload only), `workloads` carries timings of
+the other three workloads: the 32K chunk against 8 blocks, the 1M-token pass
+over 128 devices (8K chunk, 128 blocks: two fused launches), and the 32K
+chunk with its blocks streamed from pinned host memory (T_streamed,
+T_resident, T_copy, overlap efficiency, fraction of the H2D rate).
 
 Prints ONE JSON line.  `value` is causal-adjusted TFLOP/s: 4*B*H*D*(visible
 query-key pairs) per step over the measured step time.  `roofline` prices the
@@ -27,6 +35,7 @@ oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
        [--perblock] [--no-cpu-baseline] [--traffic-calib] [--no-backward] [--bwd-steps K] [--no-ffn]
+       [--no-workloads]
 """
 
 from __future__ import annotations
@@ -238,13 +247,70 @@ def ffn_measure(dev, steps, warmup):
     g = f64(y.index_select(0, idx))
     fro = float(np.linalg.norm(g - ref) / np.linalg.norm(ref))
     mx = float(np.max(np.abs(g - ref)) / np.max(np.abs(ref)))
+    # torch's own path for the same blockwise network, a stated baseline:
+    # hipBLASLt GEMMs with the bias, then a separate tanh GELU
+    import torch.nn.functional as F
+    y_t = torch.empty_like(x)
+    br = wl.block_rows
+
+    def torch_pass():
+        for r0 in range(0, wl.rows, br):
+            hid = F.gelu(F.linear(x[r0:r0 + br], w1, b1), approximate="tanh")
+            y_t[r0:r0 + br] = F.linear(hid, w2, b2)
+    for _ in range(warmup):
+        torch_pass()
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(steps):
+        torch_pass()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms_t = ev[0].elapsed_time(ev[1]) / steps
     return {
         "workload": wl.name, "ms_per_step": ms, "steps": steps, "value": f / (ms * 1e-3) / 1e12, "unit": "TFLOP/s",
         "pct_of_bf16_peak": 100.0 * f / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, "algorithmic_flop_per_step": f,
         "kernels": "gemm_bt_kernel<gelu> + gemm_bt_kernel<plain> per block",
         "parity_sampled": {"rows": len(rows), "rel_fro": fro, "max_abs_over_max": mx,
                            "pass": bool(fro <= 5e-3 and mx <= 2e-2)},
+        "torch_hipblaslt_baseline": {"ms_per_step": ms_t, "value": f / (ms_t * 1e-3) / 1e12, "unit": "TFLOP/s",
+                                     "path": "per block: F.linear (hipBLASLt, bias) -> F.gelu(tanh) -> F.linear"},
     }
+
+
+def _duration(sec: float) -> str:
+    """Seconds as a short human duration with two significant digits."""
+    for unit, div in (("h", 3600.0), ("min", 60.0), ("s", 1.0)):
+        if sec >= div or unit == "s":
+            return f"{sec / div:.2g} {unit}"
+
+
+def _single_core_oracle(x, wl, heads, rows):
+    """The same oracle on one core (BLAS limited to one thread): a smaller
+    sample of the same rows, in the same unit."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    pos = [wl.kv_pos0(j) for j in range(wl.num_blocks)]
+    k_host, v_host, q_host = x.k.cpu(), x.v.cpu(), x.q.cpu()
+    t = 0.0
+    n_vis = 0
+    with threadpool_limits(limits=1):
+        for h in heads:
+            q64 = q_host[:, :, h:h + 1, :].float().double().numpy()
+            kb = [k_host[:, j * wl.kv_len:(j + 1) * wl.kv_len, h:h + 1, :].float().double().numpy()
+                  for j in range(wl.num_blocks)]
+            vb = [v_host[:, j * wl.kv_len:(j + 1) * wl.kv_len, h:h + 1, :].float().double().numpy()
+                  for j in range(wl.num_blocks)]
+            t0 = time.perf_counter()
+            oracle.ring_attention(q64, kb, vb, wl.q_pos0, pos, wl.causal, rows=np.asarray(rows))
+            t += time.perf_counter() - t0
+    for r in rows:
+        tq = wl.q_pos0 + int(r)
+        for j in range(wl.num_blocks):
+            n_vis += wl.kv_len if not wl.causal else max(0, min(wl.kv_len, tq - wl.kv_pos0(j) + 1))
+    f = 4 * wl.head_dim * n_vis * len(heads)
+    return {"value": f / t / 1e12, "unit": "TFLOP/s", "cores": 1, "seconds": t,
+            "sample": f"{len(rows)} of the same rows x {len(heads)} head, BLAS on one thread"}
 
 
 def cpu_baseline(x, wl, o, lse, heads=None, extra_rows=94):
@@ -299,12 +365,113 @@ def cpu_baseline(x, wl, o, lse, heads=None, extra_rows=94):
         "value": value, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
         "sample": f"{len(rows)} query rows (first, last, {extra_rows} seeded) x {len(heads)} heads of the same workload, "
                   f"fp64 NumPy, {t_oracle:.1f} s; full-workload extrapolation "
-                  f"{per_pair * visible_pairs(wl) * wl.heads * wl.batch / 3600:.0f} h",
+                  f"{_duration(per_pair * visible_pairs(wl) * wl.heads * wl.batch)}",
+        "seconds": t_oracle,
+        "single_core": _single_core_oracle(x, wl, heads[:1], rows_np[:max(2, len(rows_np) // 8)]),
     }
     tol_ok = err_o <= 2e-2 and err_l <= 1e-3 and (scale_o == 0 or err_o <= 1e-2 * scale_o)
     parity = {"rows": len(rows) * len(heads), "max_abs_o": err_o, "max_rel_lse": err_l,
               "max_abs_o_over_max_o": err_o / scale_o if scale_o else 0.0, "pass": bool(tol_ok)}
     return base, parity
+
+
+def streamed_overlap(x, kb, vb, pos, o, lse, desc, ws, hk, hv, stage_k, stage_v, t_str, steps):
+    """Overlap of the host-streamed pass: its time t_str (s) against the
+    device-resident per-block pass and the H2D copies alone."""
+    import torch
+    from long_context_exact_blockwise_amd import ringattn as ra
+
+    def resident():
+        ra.ringattn_ring_fwd(desc, x.q, kb, vb, pos, o, lse, *ws)
+    for _ in range(2):
+        resident()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        resident()
+    torch.cuda.synchronize()
+    t_res = (time.perf_counter() - t1) / steps
+    nbytes = sum(t.numel() * t.element_size() for t in hk + hv)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        for i in range(len(hk)):
+            stage_k[i % 2].copy_(hk[i], non_blocking=True)
+            stage_v[i % 2].copy_(hv[i], non_blocking=True)
+    torch.cuda.synchronize()
+    t_copy = (time.perf_counter() - t1) / steps
+    eta = (t_res + t_copy - t_str) / min(t_res, t_copy)
+    return {
+        "t_streamed_ms": t_str * 1e3, "t_resident_ms": t_res * 1e3, "t_copy_ms": t_copy * 1e3,
+        "h2d_GBps": nbytes / t_copy / 1e9, "h2d_bytes": nbytes,
+        "fraction_of_h2d_bw": (nbytes / t_str) / (nbytes / t_copy),
+        "overlap_efficiency": max(0.0, min(1.0, eta)),
+        "note": "overlap = (T_resident + T_copy - T_streamed) / min(T_resident, T_copy); the PCIe-inclusive "
+                "rate is `value`; fraction_of_h2d_bw = achieved H2D rate during the streamed pass over the "
+                "copy-only rate",
+    }
+
+
+def workload_summary(dev, cfg: int, steps: int = 5, warmup: int = 2) -> dict:
+    """Timings only for another workload: the fused ring pass (its own
+    inputs, generated here), or for the host-streamed workload the
+    streamed per-block pass with its overlap figures."""
+    import torch
+    from long_context_exact_blockwise_amd import inputs
+    from long_context_exact_blockwise_amd import ringattn as ra
+    wl = inputs.CONFIGS[cfg]
+    x = inputs.make_inputs(wl, dev, seed=0)
+    order = ra.ringattn_ring_order(wl.q_idx, wl.num_blocks)
+    kb = [x.k_block(j) for j in order]
+    vb = [x.v_block(j) for j in order]
+    pos = [wl.kv_pos0(j) for j in order]
+    o = torch.empty_like(x.q)
+    lse = torch.empty((wl.batch, wl.heads, wl.q_len), dtype=torch.float32, device=dev)
+    perblock = wl.host_streamed
+    desc = ra.make_desc(x.q, kb[0], o, q_pos0=wl.q_pos0, causal=wl.causal,
+                        flags=ra.RA_FLAG_PERBLOCK if perblock else 0)
+    ws = ra.state_buffers(desc, dev) if (perblock or len(kb) > ra.RA_FUSED_MAX_BLOCKS) else (None, None, None)
+    if wl.host_streamed:
+        hk = [t.cpu().pin_memory() for t in kb]
+        hv = [t.cpu().pin_memory() for t in vb]
+        stage_k = [torch.empty_like(kb[0]).contiguous() for _ in range(2)]
+        stage_v = [torch.empty_like(vb[0]).contiguous() for _ in range(2)]
+        copy_stream = torch.cuda.Stream()
+        hdesc = ra.make_desc(x.q, hk[0], o, q_pos0=wl.q_pos0, causal=wl.causal)
+
+        def step():
+            ra.ringattn_ring_fwd(hdesc, x.q, hk, hv, pos, o, lse, *ws, kv_on_host=True, stage_k=stage_k,
+                                 stage_v=stage_v, copy_stream=copy_stream)
+    else:
+        def step():
+            ra.ringattn_ring_fwd(desc, x.q, kb, vb, pos, o, lse, *ws)
+    for _ in range(warmup):
+        step()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    f = flops(wl)
+    out = {
+        "workload": wl.name, "path": "host-streamed per-block" if perblock else "fused", "steps": steps,
+        "ms_per_step": ms, "kernel_ms_median": ev_ms[len(ev_ms) // 2], "kernel_ms_min": ev_ms[0],
+        "value": f / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "pct_of_bf16_peak": 100.0 * f / (ms * 1e-3) / 1e12 /
+        PEAK_BF16_TFLOPS, "algorithmic_flop_per_step": f,
+        "launches_per_step": None if perblock else -(-len(kb) // ra.RA_FUSED_MAX_BLOCKS),
+        "outputs_finite": bool(torch.isfinite(o.float()).all().item()),
+    }
+    if wl.host_streamed:
+        out["host_streamed"] = streamed_overlap(x, kb, vb, pos, o, lse, desc, ws, hk, hv, stage_k, stage_v,
+                                                ms * 1e-3, steps)
+    del x, kb, vb, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -318,6 +485,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=3)
     ap.add_argument("--no-ffn", action="store_true", help="skip the feedforward measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the timings of the other workloads (32K chunk, 1M tokens / 128, host-streamed)")
     ap.add_argument("--traffic-calib", action="store_true",
                     help="also run one 1 GiB plain copy kernel (byte-counter calibration)")
     args = ap.parse_args()
@@ -390,37 +559,8 @@ def main():
     finite = bool(torch.isfinite(o.float()).all().item())
 
     if wl.host_streamed:
-        # Overlap: resident per-block time, copy-only time, streamed time.
-        def resident():
-            ra.ringattn_ring_fwd(desc, x.q, kb, vb, pos, o, lse, *ws)
-        for _ in range(2):
-            resident()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            resident()
-        torch.cuda.synchronize()
-        t_res = (time.perf_counter() - t1) / args.steps
-        nbytes = sum(t.numel() * t.element_size() for t in hk + hv)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            for i in range(len(hk)):
-                stage_k[i % 2].copy_(hk[i], non_blocking=True)
-                stage_v[i % 2].copy_(hv[i], non_blocking=True)
-        torch.cuda.synchronize()
-        t_copy = (time.perf_counter() - t1) / args.steps
-        t_str = ms_step * 1e-3
-        eta = (t_res + t_copy - t_str) / min(t_res, t_copy)
-        extra["host_streamed"] = {
-            "t_streamed_ms": t_str * 1e3, "t_resident_ms": t_res * 1e3, "t_copy_ms": t_copy * 1e3,
-            "h2d_GBps": nbytes / t_copy / 1e9, "h2d_bytes": nbytes,
-            "fraction_of_h2d_bw": (nbytes / t_str) / (nbytes / t_copy),
-            "overlap_efficiency": max(0.0, min(1.0, eta)),
-            "note": "overlap = (T_resident + T_copy - T_streamed) / min(T_resident, T_copy); the PCIe-inclusive "
-                    "rate is `value`; fraction_of_h2d_bw = achieved H2D rate during the streamed pass over the "
-                    "copy-only rate",
-        }
+        extra["host_streamed"] = streamed_overlap(x, kb, vb, pos, o, lse, desc, ws, hk, hv, stage_k, stage_v,
+                                                  ms_step * 1e-3, args.steps)
 
     probed = probe_peak(dev) if wl.dtype == "bf16" else None
 
@@ -486,6 +626,12 @@ def main():
         result["ffn"] = ffn_measure(dev, 10, 2)
         if probed:
             result["ffn"]["pct_of_probed_peak"] = 100.0 * result["ffn"]["value"] / probed
+    if not args.no_workloads and args.workload == 3:
+        # the timed workload's tensors are no longer needed
+        del x, kb, vb, o, lse, ws
+        torch.cuda.empty_cache()
+        result["workloads"] = {name: workload_summary(dev, cfg) for name, cfg in
+                               (("chunk32k_p8", 2), ("tokens1m_p128", 4), ("chunk32k_p8_host_streamed", 5))}
     print(json.dumps(result), flush=True)
 
 
