@@ -94,14 +94,16 @@ constexpr float kPLim = 4096.0f;
 // differs from an exactly normalised bf16-P average by at most the bf16
 // rounding of P).  The other 32 keys of the tile sit in the lane 32 away.
 __device__ __forceinline__ float softmax_exp(const f32x16 (&s)[2], float c2, float mref, bf16x2 (&p)[16]) {
-  float rsq[4] = {0.f, 0.f, 0.f, 0.f};
+  float rsq[4];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int e = 2 * q;
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][e & 15], c2, -mref));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e >> 4][(e & 15) + 1], c2, -mref));
     p[q] = bf16x2{(__bf16)p0, (__bf16)p1};
-    rsq[q & 3] += p0 + p1;
+    // (the four partial sums start from the first pairs, not from 0: x + 0
+    // cannot be folded away, since -0 + 0 is +0)
+    rsq[q & 3] = q < 4 ? p0 + p1 : rsq[q & 3] + (p0 + p1);
   }
   return (rsq[0] + rsq[1]) + (rsq[2] + rsq[3]);
 }
@@ -349,8 +351,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     seek(ck, 1);
     seek(cv, 2);
     int kidx = 0, vidx = 0;
+    // (slots are never negative: the unsigned remainder is one AND)
+    auto slot_dst = [&](int s) -> uint32_t { return lds0 + ((uint32_t)s % kBufs) * C::SLOT_BYTES; };
     auto copy_slot = [&](int s) {
-      const uint32_t dst = lds0 + (uint32_t)((s % kBufs) * C::SLOT_BYTES);
+      const uint32_t dst = slot_dst(s);
       if (ck.t != ck.ragged && cv.t != cv.ragged) {
         lds_dma_slot<DPW>(ck.src, cv.src, dkj, dvj, dst);
       } else {
@@ -366,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
         ++vidx;
       }
     };
-    auto slot_at = [&](int s) -> uint32_t { return lds_base + (uint32_t)((s % kBufs) * C::SLOT_BYTES); };
+    auto slot_at = [&](int s) -> uint32_t { return lds_base + ((uint32_t)s % kBufs) * C::SLOT_BYTES; };
 
     // ---- per-lane LDS byte offsets inside a slot.  K: row l32 (+32 per key
     // block), chunk 2ks+hf: kofs[ks].  V^T via transpose loads: in each
@@ -454,12 +458,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
     // One tile: S of tile t in sc (softmax now), S of t+1 into sn, P of t-1
     // in pp (P.V now), P of t into pc.  The loop runs two tiles per trip
     // with the register sets swapping roles, so no copies rotate them.
-    auto tile = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x2 (&pp)[16], bf16x2 (&pc)[16]) {
-      copy_slot(t + kBufs);
+    //
+    // Fast tiles (kFast) are the tiles of a run (see fast_run): neither copy
+    // cursor reaches the end of its block, a ragged tile or the last tile,
+    // and the compute tile needs no mask, so the tile issues its copies
+    // straight from the cursors, and its only bookkeeping is two pointer
+    // increments placed before the barrier, where waves wait anyway.  The
+    // tile counters of the cursors are advanced once per run.  Checked tiles
+    // step every cursor with all its tests (block ends, ragged tiles, the
+    // clamp at the last tile) and apply the mask where a tile needs one.
+    auto tile = [&](auto fast_tag, int t, f32x16 (&sc)[2], f32x16 (&sn)[2], const bf16x2 (&pp)[16],
+                    bf16x2 (&pc)[16]) {
+      constexpr bool kFast = decltype(fast_tag)::value;
+      if constexpr (kFast) {
+        lds_dma_slot<DPW>(ck.src, cv.src, dkj, dvj, slot_dst(t + kBufs));
+      } else {
+        copy_slot(t + kBufs);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // mask keys past the block end and (causal) keys after this lane's row:
       // key k of the tile is live iff k < thr
-      if (cs.t == cs.ragged || (a.causal && cs.rel + (BN - 1) > wrow0)) {
+      if (!kFast && (cs.t == cs.ragged || (a.causal && cs.rel + (BN - 1) > wrow0))) {
         int lim = cs.t == cs.ragged ? cs.len - cs.t * BN : BN;
         if (a.causal) {
           const int lc = myrow - cs.rel + 1;
@@ -490,18 +509,59 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(AttnArgs a, Bloc
         rs = softmax_redo<C::DB>(sc, c2s, m2, lpart, acc, pc);
       }
       lpart += rs;
+      if constexpr (kFast) {
+        ck.src += tile_bytes_g;
+        cv.src += tile_bytes_g;
+      }
       // slot t+2 (read by tile t+1) has landed; kBufs-2 newer slots may fly
       wait_vm<(kBufs - 2) * 2 * DPW>();
       wg_barrier();
-      step(cs, 0);
+      if constexpr (!kFast) step(cs, 0);
     };
+    // Tiles from t on that can run as fast tiles: each copies the tiles
+    // under the copy cursors and then steps them inside their blocks (a
+    // ragged tile is always a block's last), without reaching the last tile;
+    // the compute tiles stay inside their block and before the first tile
+    // this wave must mask (causal: the first whose last key lies past the
+    // wave's first row).
+    auto fast_run = [&](int t) -> int {
+      int64_t r = (int64_t)ck.n - 1 - ck.t;
+      r = r < (int64_t)n_tiles - 1 - kidx ? r : (int64_t)n_tiles - 1 - kidx;
+      r = r < (int64_t)cv.n - 1 - cv.t ? r : (int64_t)cv.n - 1 - cv.t;
+      r = r < (int64_t)n_tiles - 1 - vidx ? r : (int64_t)n_tiles - 1 - vidx;
+      r = r < (int64_t)cs.n - 1 - cs.t ? r : (int64_t)cs.n - 1 - cs.t;
+      if (a.causal) {
+        const int64_t room = (int64_t)wrow0 - (BN - 1) - cs.rel;  // tile j is unmasked iff rel_j + 63 <= wrow0
+        const int64_t nm = room < 0 ? 0 : room / BN + 1;
+        r = r < nm ? r : nm;
+      }
+      r = r < (int64_t)n_tiles - t ? r : (int64_t)n_tiles - t;
+      return r < 0 ? 0 : (int)r;
+    };
+    constexpr std::true_type kFastTile{};
+    constexpr std::false_type kCheckedTile{};
     int t = 0;
-    for (; t + 1 < n_tiles; t += 2) {
-      tile(t, s_cur, s_nxt, p_prev, p_cur);
-      tile(t + 1, s_nxt, s_cur, p_cur, p_prev);
+    while (t + 1 < n_tiles) {
+      const int run = fast_run(t) & ~1;
+      for (int i = 0; i < run; i += 2) {
+        tile(kFastTile, t + i, s_cur, s_nxt, p_prev, p_cur);
+        tile(kFastTile, t + i + 1, s_nxt, s_cur, p_cur, p_prev);
+      }
+      ck.t += run;
+      kidx += run;
+      cv.t += run;
+      vidx += run;
+      cs.t += run;
+      cs.rel += run * BN;
+      t += run;
+      if (t + 1 < n_tiles) {
+        tile(kCheckedTile, t, s_cur, s_nxt, p_prev, p_cur);
+        tile(kCheckedTile, t + 1, s_nxt, s_cur, p_cur, p_prev);
+        t += 2;
+      }
     }
     if (t < n_tiles) {
-      tile(t, s_cur, s_nxt, p_prev, p_cur);
+      tile(kCheckedTile, t, s_cur, s_nxt, p_prev, p_cur);
 #pragma unroll
       for (int q = 0; q < 16; ++q) p_prev[q] = p_cur[q];  // the last tile's P, for the final P.V
     }

@@ -92,6 +92,29 @@ def test_block_order_does_not_matter():
         assert torch.allclose(l, outs[0][1], atol=1e-3, rtol=1e-4)
 
 
+@pytest.mark.parametrize("causal,valid", [(True, None), (False, None), (True, (2048, 1999, 2048, 1037))],
+                         ids=["causal", "noncausal", "causal_ragged"])
+def test_long_tile_runs(causal, valid):
+    """2048 rows against 4 blocks of 2048 keys (32 tiles each, K and V in
+    separate allocations), in ring order: most tiles run in long stretches
+    with no cursor test, broken by block ends, ragged last tiles and the
+    causal diagonal."""
+    wl = small(q_len=2048, kv_len=2048, p=4, causal=causal, q_idx=3)
+    x = inputs.make_inputs(wl, cuda(), seed=12)
+    order = ra.ringattn_ring_order(3, 4)
+    if valid is None:
+        print(_check(x, order=order))
+        return
+    from tests.test_gpu_varlen_striped import _oracle_varlen, _poison_padding
+    _poison_padding(x, valid)
+    o, lse = ra.ring_forward(x.q, [x.k_block(j) for j in order], [x.v_block(j) for j in order],
+                             [wl.kv_pos0(j) for j in order], q_pos0=wl.q_pos0, causal=causal,
+                             kv_valid=[valid[j] for j in order])
+    torch.cuda.synchronize()
+    ref_o, ref_l = _oracle_varlen(x, list(valid))
+    print(compare(*gpu_rows(o, lse), ref_o, ref_l, "bf16", "long tile runs, ragged"))
+
+
 def test_fused_matches_perblock():
     x = inputs.make_inputs(small(q_len=512, kv_len=320, p=3, q_idx=1), cuda(), seed=9)
     o1, l1 = run_hip(x)
