@@ -303,31 +303,41 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK and dV in one pass, split over wave pairs: a workgroup owns 128 keys;
 // wave w (0-3, the P side) and wave w+4 (the dS side) share a SIMD and the
-// same 32 keys.  For query tile t the P side forms S = Q K^T and P (from the
-// forward's LSE), stores P as bf16 in LDS and accumulates dV^T += dO^T P; one
-// tile later the dS side forms dP = dO V^T, reads that P (the value dV used),
-// forms dS = P (dP - delta) and accumulates dK^T += Q^T dS.  Both sides hold
-// the same key in the same lane and the scores in the same accumulator
-// layout, so the hand-over is a plain per-lane copy.  Four LDS stages: tile
-// t (P side), t-1 (dS side), t+1 landed, t+2 in flight; two P buffers
-// alternate between trips.
-constexpr int kPairStages = 4;
-constexpr int BKP = 128;  // keys per workgroup (32 per wave pair)
+// same 32 keys.  For query tile t (64 rows) the P side forms S = Q K^T and P
+// (from the forward's LSE), stores P as bf16 in LDS and accumulates
+// dV^T += dO^T P; one trip later the dS side forms dP = dO V^T, reads that P
+// (the value dV used), forms dS = P (dP - delta) and accumulates
+// dK^T += Q^T dS.  Both sides hold the same key in the same lane and the
+// scores in the same accumulator layout, so the hand-over is a plain per-lane
+// copy.  Each stage holds the tile's Q and dO rows once, in the placement
+// both read kinds take without bank conflicts (u_off): row reads for S and
+// dP, transpose reads for dO^T and Q^T.  Three stages (tile t for the P side,
+// t-1 for the dS side, t+1 landing) and two P buffers that alternate between
+// trips.  Every wave copies one contiguous run of 1 KiB chunks per stage
+// under one M0 value; the first wave of each half also copies the tile's LSE
+// (P side) or delta (dS side) under the same M0, in the 256 bytes in front of
+// its run.
+constexpr int BQK = 64;      // dK/dV kernel: query rows per tile
+constexpr int kKvStages = 3;
+constexpr int BKP = 128;     // keys per workgroup (32 per wave pair)
 
 template <int D>
-struct PairStage {
-  static constexpr int QT = BQT * D * 2;
-  // Q rows, dO^T (transpose placement), dO rows, Q^T (transpose placement),
-  // then LSE and delta of the tile's 32 rows
-  static constexpr int LSE_OFF = 4 * QT;
-  static constexpr int DLT_OFF = 4 * QT + 256;
-  static constexpr int BYTES = 4 * QT + 512;
-  static constexpr int PX_OFF = kPairStages * BYTES;  // two P buffers: 4 pairs x 64 lanes x 32 bytes
-  static constexpr int PX_BYTES = 4 * 64 * 32;
+struct KvStage {
+  static constexpr int ROWB = 2 * D;
+  static constexpr int TB = BQK * ROWB;       // bytes of a 64-row tile of Q or dO
+  // LSE[64], Q tile, delta[64], dO tile
+  static constexpr int LSE_OFF = 0;
+  static constexpr int Q_OFF = 256;
+  static constexpr int DLT_OFF = 256 + TB;
+  static constexpr int DO_OFF = 512 + TB;
+  static constexpr int BYTES = 512 + 2 * TB;
+  static constexpr int PX_OFF = kKvStages * BYTES;
+  static constexpr int PX_PAIR = BQK * 32 * 2;  // bf16 P of one pair: 64 rows x 32 keys
+  static constexpr int PX_BYTES = 4 * PX_PAIR;
   static constexpr int LDS = PX_OFF + 2 * PX_BYTES;
-  static constexpr int TOTAL = 4 * QT / 1024;
-  static constexpr int CPW = TOTAL / kBWaves;
-  static_assert(TOTAL % kBWaves == 0, "copies per wave");
+  static constexpr int CPT = TB / 1024;          // 1 KiB chunks per tile
+  static constexpr int CPW = 2 * CPT / kBWaves;  // per wave per stage: 4 (D = 128) or 2 (D = 64)
+  static_assert(CPW == 4 || CPW == 2, "copies per wave");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -335,7 +345,7 @@ struct PairStage {
 template <int D>
 __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
   using C = BCfg<D>;
-  using S = PairStage<D>;
+  using S = KvStage<D>;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int n_kt = (int)((a.kv_len + BKP - 1) / BKP);
   const int n_work = a.batch * a.heads * n_kt;
@@ -362,8 +372,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
     if (r_min < 0) r_min = 0;
     if (r_min >= a.q_len) return;
   }
-  const int n_qt = (int)((a.q_len + BQT - 1) / BQT);
-  const int qt0 = (int)(r_min / BQT);
+  const int n_qt = (int)((a.q_len + BQK - 1) / BQK);
+  const int qt0 = (int)(r_min / BQK);
 
   // K fragments (role 0) or V fragments (role 1) of this lane's key
   bf16x8 fr[C::KS];
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
   }
   wait_vm<0>();  // the register loads above, before any copy is in flight
   const float c2 = a.scale * kLog2e;
-  const int64_t first_row = a.causal ? a.kv_pos0 + c - a.q_pos0 : 0;
+  const int64_t first_row = a.causal ? a.kv_pos0 + c - a.q_pos0 : 0;  // rows >= first_row see key c
   f32x16 acc[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -392,133 +402,184 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
   const char* osrc = (const char*)a.dout + (b * a.q_sb + h * a.q_sh) * 2;
   const char* lse_bh = (const char*)(a.lse + ((int64_t)b * a.heads + h) * a.q_len);
   const char* dl_bh = (const char*)(a.delta + ((int64_t)b * a.heads + h) * a.q_len);
-  auto stage = [&](int t) -> uint32_t { return base + (t % kPairStages) * S::BYTES; };
+  auto stage = [&](int t) -> uint32_t { return base + ((uint32_t)t % kKvStages) * S::BYTES; };
+
+  // ---- copies: wave w takes chunks CPW w .. CPW w + CPW - 1 of the stage's
+  // 2 CPT chunks (Q tile, then dO tile): a contiguous run, one M0.  Per-lane
+  // global offsets do not depend on the tile; each has its instruction offset
+  // taken out.  Waves 0 and 4 (first of the Q and dO runs) also copy LSE and
+  // delta (64 rows, 4 bytes per lane) into the 256 bytes in front of the run.
+  const int w_tile = (S::CPW * wave) / S::CPT;  // 0: Q, 1: dO
+  const char* w_src = w_tile == 0 ? qsrc : osrc;
+  const bool w_lead = (S::CPW * wave) % S::CPT == 0;  // waves 0 and 4
+  const char* w_dsrc = w_tile == 0 ? lse_bh : dl_bh;
+  const uint32_t w_run = (w_tile == 0 ? S::Q_OFF : S::DO_OFF) + ((S::CPW * wave) % S::CPT) * 1024;
+  uint32_t w_off[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < S::CPW; ++j) {
+    const int p = ((S::CPW * wave) % S::CPT + j) * 1024 + lane * 16;
+    const int rw = p / S::ROWB;
+    const int pc = (p % S::ROWB) / 16;
+    const int lc = pc ^ u_swz<D>(rw);  // the logical chunk that the placement puts here
+    // (>= 0: chunk j's rows start at or after byte 1 KiB j of the source, a
+    // row being >= 128 bytes; the lead waves' extra 256 goes on the base)
+    w_off[j] = (uint32_t)(rw * qrow_bytes + lc * 16) - 1024u * j;
+  }
   auto issue = [&](int t) {
     const uint32_t st = stage(t);
-    const int64_t row = (int64_t)t * BQT + l32;
-    const uint32_t roff = (uint32_t)((row < a.q_len ? row : a.q_len - 1) * 4);
-    if (wave == 0) lds_dma4(lse_bh, roff, st + S::LSE_OFF);
-    if (wave == 1) lds_dma4(dl_bh, roff, st + S::DLT_OFF);
-    const int64_t go = (int64_t)t * BQT * qrow_bytes;
-    const int valid = (int)(a.q_len - (int64_t)t * BQT);
-    const int per_copy = S::QT / 1024;
+    const int64_t row0 = (int64_t)t * BQK;
+    const int64_t go = row0 * qrow_bytes;
+    const int valid = (int)(a.q_len - row0);
+    if (valid >= BQK) {
+      if (w_lead) {  // the runs' instruction offsets are 256 + 1 KiB j: the global base moves 256 down
+        if constexpr (S::CPW == 4)
+          lds_dma_1x4(w_dsrc + row0 * 4, (uint32_t)lane * 4, w_src + go - 256, w_off, st + w_run - 256);
+        else
+          lds_dma_1x2(w_dsrc + row0 * 4, (uint32_t)lane * 4, w_src + go - 256, w_off, st + w_run - 256);
+      } else {
+        if constexpr (S::CPW == 4)
+          lds_dma_x4(w_src + go, w_off, st + w_run);
+        else
+          lds_dma_x2(w_src + go, w_off, st + w_run);
+      }
+      return;
+    }
+    // last, partial tile: rows past the chunk's end re-read its last row
+    if (w_lead) {
+      const int rr = lane < valid ? lane : valid - 1;
+      lds_dma4(w_dsrc + row0 * 4, (uint32_t)rr * 4, st + w_run - 256);
+    }
 #pragma unroll
     for (int j = 0; j < S::CPW; ++j) {
-      const int g = wave + kBWaves * j;
-      const int cp = g / per_copy;  // 0: Q rows, 1: dO^T, 2: dO rows, 3: Q^T
-      const int cc = g - cp * per_copy;
-      const int p = cc * 1024 + lane * 16;
-      const int rw = p / (D * 2);
-      const int cs = (p % (D * 2)) / 16;
-      const bool tr = cp & 1;
-      const int col = (tr ? v_off<D>(rw, cs) : k_off<D>(rw, cs)) / 16 - rw * (D / 8);
+      const int p = ((S::CPW * wave) % S::CPT + j) * 1024 + lane * 16;
+      const int rw = p / S::ROWB;
+      const int pc = (p % S::ROWB) / 16;
+      const int lc = pc ^ u_swz<D>(rw);
       const int rr = rw < valid ? rw : valid - 1;
-      const char* src = (cp == 1 || cp == 2) ? osrc + go : qsrc + go;
-      lds_dma16(src, (uint32_t)(rr * qrow_bytes + col * 16), st + cp * S::QT + cc * 1024);
+      lds_dma16(w_src + go, (uint32_t)(rr * qrow_bytes + lc * 16), st + w_run + j * 1024);
     }
   };
-  const int vA = tr_base<D>(lane);
-  const uint32_t px_lane = base + S::PX_OFF + pair * (64 * 32) + lane * 32;  // this lane's 32 bytes of P
+
+  // ---- per-lane LDS offsets.  Row reads (S = Q K^T, dP = dO V^T): row l32
+  // (+32: an immediate, u depends on the row mod 16), chunk 2 ks + hf.
+  // Transpose reads (dO^T, Q^T): rows key0 (lo) and key0 + 8 (hi) of each
+  // 16-row step (steps are immediates), column block db by XOR with 64 db.
+  int rofs[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) rofs[ks] = u_off<D>(l32, 2 * ks + hf);
+  int tr_lo, tr_hi;
+  {
+    const int g4 = lane >> 4, tt = (lane >> 2) & 3, ss = lane & 3;
+    const int key0 = 4 * (g4 >> 1) + tt;
+    const int c0 = 2 * (g4 & 1) + (ss >> 1);
+    tr_lo = u_off<D>(key0, c0) + (ss & 1) * 8;
+    tr_hi = u_off<D>(key0 + 8, c0) + (ss & 1) * 8;
+  }
+  auto tr_frag_u = [&](uint32_t tile, int db, int row) -> bf16x8 {
+    const uint32_t lo = tile + ((uint32_t)tr_lo ^ (64u * db)) + row * S::ROWB;
+    const uint32_t hi = tile + ((uint32_t)tr_hi ^ (64u * db)) + row * S::ROWB;
+    const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)lo);
+    const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)hi);
+    return __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // P hand-over: this lane's 64 bytes as four 16-byte pieces, piece j at
+  // 1 KiB j + 16 lane (consecutive lanes on consecutive banks)
+  const uint32_t px_lane = base + S::PX_OFF + pair * S::PX_PAIR + lane * 16;
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_w;
+  typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 
   issue(qt0);
-  if (qt0 + 1 < n_qt) {
-    issue(qt0 + 1);
-    wait_vm<S::CPW>();
-  } else {
-    wait_vm<0>();
-  }
+  wait_vm<0>();
   wg_barrier();
-  const int n_iter = n_qt - qt0 + 1;  // the last trip serves only the dK side
+  const int n_iter = n_qt - qt0 + 1;  // the last trip serves only the dS side
   for (int i = 0; i < n_iter; ++i) {
     const int t = qt0 + i;
-    if (t + 2 < n_qt) issue(t + 2);
+    if (t + 1 < n_qt) issue(t + 1);
     const int tw = role == 0 ? t : t - 1;  // this wave's tile
     if (tw >= qt0 && tw < n_qt) {
       const uint32_t st = stage(tw);
-      const int64_t row_t0 = (int64_t)tw * BQT;
-      const int lo = key_ok ? clamp_i(first_row - row_t0, 0, BQT) : BQT;
-      const int hi = clamp_i(a.q_len - row_t0, 0, BQT);
-      // S = Q K^T (role 0) or dP = dO V^T (role 1)
-      f32x16 r = f32x16{};
-      const uint32_t rows = st + (role == 0 ? 0 : 2 * S::QT);
+      const int64_t row_t0 = (int64_t)tw * BQK;
+      const int lo = key_ok ? clamp_i(first_row - row_t0, 0, BQK) : BQK;  // rows [lo, hi) of the tile see the key
+      const int hi = clamp_i(a.q_len - row_t0, 0, BQK);
+      // S = Q K^T (role 0) or dP = dO V^T (role 1), rows 0-31 and 32-63
+      f32x16 r0 = f32x16{}, r1 = f32x16{};
+      const uint32_t rows = st + (role == 0 ? S::Q_OFF : S::DO_OFF);
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rows + k_off<D>(l32, 2 * ks + hf)), fr[ks],
-                                                    r, 0, 0, 0);
-      bf16x2 x[8];
+      for (int ks = 0; ks < C::KS; ++ks) {
+        r0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rows + rofs[ks]), fr[ks], r0, 0, 0, 0);
+        r1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rows + rofs[ks] + 32 * S::ROWB), fr[ks], r1,
+                                                     0, 0, 0);
+      }
+      bf16x2 x[16];  // P (role 0) or dS (role 1) as bf16 pairs: rows of r0, then of r1
       if (role == 0) {
-        // P = exp2(S c - LSE2[row]), masked; kept for the dK side.  Where
-        // every row of the tile sees every key of the wave (wave-uniform),
-        // no position test is needed, and exp2(-|x|) covers rows without a
-        // visible key: x = S c - LSE2 <= 0 for a row's visible keys (LSE is
-        // at least each visible score), while LSE = -inf makes x = +inf and
-        // P = 0; the sign and absolute value are free operand modifiers.
-        const bool full = hi == BQT && __all(lo == 0);
+        // P = exp2(S c - LSE2[row]), masked.  Where every row of the tile
+        // sees every key of the wave (wave-uniform), no position test is
+        // needed, and exp2(-|x|) covers rows without a visible key: x =
+        // S c - LSE2 <= 0 for a row's visible keys (LSE is at least each
+        // visible score), while LSE = -inf makes x = +inf and P = 0.
+        const bool full = hi == BQK && __all(lo == 0);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
-          const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (8 * g + 4 * hf) * 4);
-          float v[4];
-          if (full) {
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const f32x16& r = h2 == 0 ? r0 : r1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              v[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)));
-          } else {
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (32 * h2 + 8 * g + 4 * hf) * 4);
+            float v[4];
+            if (full) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int row = acc_row(4 * g + j, hf);
-              const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
-              v[j] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)) : 0.f;
+              for (int j = 0; j < 4; ++j)
+                v[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)));
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int row = 32 * h2 + acc_row(4 * g + j, hf);
+                const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
+                v[j] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)) : 0.f;
+              }
             }
+            x[8 * h2 + 2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+            x[8 * h2 + 2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
           }
-          x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
-          x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
         }
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
         const uint32_t px = px_lane + (i & 1) * S::PX_BYTES;
-        *(lds_u32x4*)(size_t)px = u32x4{__builtin_bit_cast(uint32_t, x[0]), __builtin_bit_cast(uint32_t, x[1]),
-                                        __builtin_bit_cast(uint32_t, x[2]), __builtin_bit_cast(uint32_t, x[3])};
-        *(lds_u32x4*)(size_t)(px + 16) = u32x4{__builtin_bit_cast(uint32_t, x[4]), __builtin_bit_cast(uint32_t, x[5]),
-                                               __builtin_bit_cast(uint32_t, x[6]), __builtin_bit_cast(uint32_t, x[7])};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(lds_bf16x8_w*)(size_t)(px + 1024 * j) = pack8(x, 4 * j);
       } else {
         // dS = P (dP - delta[row]), P written by the pair's other wave last trip
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        typedef __attribute__((address_space(3))) const u32x4 lds_u32x4c;
         const uint32_t px = px_lane + ((i - 1) & 1) * S::PX_BYTES;
-        const u32x4 w0 = *(lds_u32x4c*)(size_t)px;
-        const u32x4 w1 = *(lds_u32x4c*)(size_t)(px + 16);
-        const uint32_t pw[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
-          const f32x4 d4 = *(lds_f32x4*)(size_t)(st + S::DLT_OFF + (8 * g + 4 * hf) * 4);
-          const bf16x2 pa = __builtin_bit_cast(bf16x2, pw[2 * g]);
-          const bf16x2 pb = __builtin_bit_cast(bf16x2, pw[2 * g + 1]);
-          const float pv[4] = {(float)pa[0], (float)pa[1], (float)pb[0], (float)pb[1]};
-          float v[4];
+        for (int j = 0; j < 4; ++j) {
+          // (read as bf16 elements: extracting bf16 pairs from bit-cast
+          // 32-bit words is miscompiled by this toolchain, which keeps one
+          // word of four)
+          const bf16x8 w = *(lds_bf16x8*)(size_t)(px + 1024 * j);
+          const int h2 = j >> 1, g0 = 2 * (j & 1);
+          const f32x16& r = h2 == 0 ? r0 : r1;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[j] = pv[j] * (r[4 * g + j] - d4[j]);
-          x[2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
-          x[2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
+          for (int gg = 0; gg < 2; ++gg) {
+            const int g = g0 + gg;
+            const f32x4 d4 = *(lds_f32x4*)(size_t)(st + S::DLT_OFF + (32 * h2 + 8 * g + 4 * hf) * 4);
+            const float pv[4] = {(float)w[4 * gg], (float)w[4 * gg + 1], (float)w[4 * gg + 2], (float)w[4 * gg + 3]};
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = pv[q] * (r[4 * g + q] - d4[q]);
+            x[8 * h2 + 2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+            x[8 * h2 + 2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
+          }
         }
       }
-      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1)
-      const uint32_t trl = st + (role == 0 ? S::QT : 3 * S::QT);
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1): four 16-row steps
+      const uint32_t trl = st + (role == 0 ? S::DO_OFF : S::Q_OFF);
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
+      for (int tp = 0; tp < 4; ++tp) {
         const bf16x8 xf = pack8(x, 4 * tp);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(trl + (vA ^ (64 * db)), 16 * tp), xf, acc[db],
-                                                            0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_u(trl, db, 16 * tp), xf, acc[db], 0, 0, 0);
       }
     }
-    if (t + 2 < n_qt)
-      wait_vm<S::CPW>();  // tile t+1 landed; t+2 may be in flight
-    else
-      wait_vm<0>();
-    wait_lds();  // the P just written, before the other wave of the pair reads it
+    wait_vm<0>();  // tile t+1 landed
+    wait_lds();    // the P just written, before the other wave of the pair reads it
     wg_barrier();
   }
   if (!key_ok) return;
@@ -561,13 +622,13 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t s) {
   static bool attr_done = false;  // set once per instantiation; the attribute is idempotent
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       PairStage<D>::LDS);
+                                       KvStage<D>::LDS);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const int64_t nk = (int64_t)a.batch * a.heads * ((a.kv_len + BKP - 1) / BKP);
   if (nk > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(((nk + 7) / 8) * 8)), dim3(kBThreads), PairStage<D>::LDS,
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(((nk + 7) / 8) * 8)), dim3(kBThreads), KvStage<D>::LDS,
                        s, a);
   return hipGetLastError();
 }

@@ -35,6 +35,22 @@ __device__ __forceinline__ int v_off(int key, int c) {
   return key * (D * 2) + cs * 16;
 }
 
+// One placement for both read kinds: chunk c of row r goes to chunk
+// c ^ u(r), u a bit permutation of the row's low bits (D = 128: u = 4 (r & 3)
+// + ((r >> 2) & 3); D = 64: u = 4 ((r >> 1) & 1) + ((r >> 2) & 3)).  Sixteen
+// consecutive rows read at one chunk column (16-byte row reads) and the 4
+// rows x 4 chunks a transpose read takes per half-wave both land on distinct
+// banks of the 64.  u depends on r mod 16 only, so row offsets that are
+// multiples of 16 are instruction immediates.
+template <int D>
+__device__ __forceinline__ int u_swz(int r) {
+  return D == 128 ? (4 * (r & 3) + ((r >> 2) & 3)) : (4 * ((r >> 1) & 1) + ((r >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int u_off(int row, int c) {
+  return row * (D * 2) + (c ^ u_swz<D>(row)) * 16;
+}
+
 __device__ __forceinline__ float pair_max(float x) {
   // max(x[lane], x[lane ^ 32]) on every lane
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -86,6 +102,98 @@ __device__ __forceinline__ void lds_dma4(const char* base, uint32_t voff, uint32
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory");
+}
+
+// Four direct global->LDS copies of 16 bytes per lane under one M0: copy j
+// lands lane i's bytes at LDS byte lds_addr + 1 KiB j + 16 i from global
+// base + off[j] + 1 KiB j (the instruction offset moves both addresses, so
+// off[j] is the lane's global offset with 1 KiB j taken out).  base and
+// lds_addr are wave-uniform.
+__device__ __forceinline__ void lds_dma_x4(const char* base, const uint32_t (&off)[4], uint32_t lds_addr) {
+  const uint64_t bv = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %6\n\t"
+      "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, %6 offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, %6 offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(bs)
+      : "memory");
+}
+
+// The same with one 4-byte copy first: lane i's dword lands at lds_addr + 4 i
+// from global dbase + doff (256 bytes for the wave), then copy j lands at
+// lds_addr + 256 + 1 KiB j from base + off[j] + 256 + 1 KiB j.
+__device__ __forceinline__ void lds_dma_1x4(const char* dbase, uint32_t doff, const char* base, const uint32_t (&off)[4],
+                                            uint32_t lds_addr) {
+  const uint64_t dv = (uint64_t)dbase, bv = (uint64_t)base;
+  const uint32_t dlo = __builtin_amdgcn_readfirstlane((uint32_t)dv);
+  const uint32_t dhi = __builtin_amdgcn_readfirstlane((uint32_t)(dv >> 32));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t ds = ((uint64_t)dhi << 32) | dlo, bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %5, %7\n\t"
+      "global_load_lds_dwordx4 %1, %8 offset:256\n\t"
+      "global_load_lds_dwordx4 %2, %8 offset:1280\n\t"
+      "global_load_lds_dwordx4 %3, %8 offset:2304\n\t"
+      "global_load_lds_dwordx4 %4, %8 offset:3328\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(doff), "s"(__builtin_amdgcn_readfirstlane(lds_addr)),
+        "s"(ds), "s"(bs)
+      : "memory");
+}
+// Two-copy forms (D = 64: two 1 KiB chunks per wave).
+__device__ __forceinline__ void lds_dma_x2(const char* base, const uint32_t (&off)[4], uint32_t lds_addr) {
+  const uint64_t bv = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %4\n\t"
+      "global_load_lds_dwordx4 %2, %4 offset:1024\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(bs)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma_1x2(const char* dbase, uint32_t doff, const char* base, const uint32_t (&off)[4],
+                                            uint32_t lds_addr) {
+  const uint64_t dv = (uint64_t)dbase, bv = (uint64_t)base;
+  const uint32_t dlo = __builtin_amdgcn_readfirstlane((uint32_t)dv);
+  const uint32_t dhi = __builtin_amdgcn_readfirstlane((uint32_t)(dv >> 32));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
+  const uint64_t ds = ((uint64_t)dhi << 32) | dlo, bs = ((uint64_t)hi << 32) | lo;
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %3, %5\n\t"
+      "global_load_lds_dwordx4 %1, %6 offset:256\n\t"
+      "global_load_lds_dwordx4 %2, %6 offset:1280\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off[0]), "v"(off[1]), "v"(doff), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(ds), "s"(bs)
       : "memory");
 }
 
