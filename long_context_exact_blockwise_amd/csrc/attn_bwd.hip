@@ -57,62 +57,14 @@ struct BCfg {
   static constexpr int ROWB = D * 2;
   static constexpr int KT = BKN * ROWB;        // bytes of a 64-key tile
   static constexpr int QT = BQT * ROWB;        // bytes of a 32-row tile
-  // dq stage: K rows (row-read placement), K (transpose-read placement), V rows
-  static constexpr int DQ_STAGE = 3 * KT;
+  // dq stage: K (u_off placement: row reads for S, transpose reads for dQ),
+  // V rows (row-read placement)
+  static constexpr int DQ_STAGE = 2 * KT;
   static constexpr int DQ_LDS = kStages * DQ_STAGE;
   static constexpr int DQ_CPW = DQ_STAGE / 1024 / kBWaves;  // 1 KiB copies per wave per tile
   static_assert(DQ_STAGE % (1024 * kBWaves) == 0, "copies per wave");
   static_assert(DQ_LDS <= 160 * 1024, "LDS budget");
 };
-
-// Issue this wave's share of the copies of one stage: NCOPY row-major tiles of
-// `nrows` rows each (tile j from srcs[j], rows at row_bytes apart), placed
-// back to back at dst with the row-read placement (k_off) or, where bit j of
-// tr_mask is set, the transpose-read placement (v_off).  Rows at or past
-// `valid` re-read row valid-1 (their values are masked out later).  Every
-// wave issues exactly CPW copies, so one vmcnt bound covers every wave.
-template <int D, int NCOPY, int CPW>
-__device__ __forceinline__ void copy_stage(const char* const (&srcs)[NCOPY], int tr_mask, int64_t row_bytes,
-                                           int valid, uint32_t dst, int nrows, int wave, int lane) {
-  const int per_copy = nrows * D * 2 / 1024;
-#pragma unroll
-  for (int j = 0; j < CPW; ++j) {
-    const int g = wave + kBWaves * j;
-    const int cp = g / per_copy;
-    const int c = g - cp * per_copy;
-    const int p = c * 1024 + lane * 16;
-    const int row = p / (D * 2);
-    const int cs = (p % (D * 2)) / 16;
-    const bool tr = (tr_mask >> cp) & 1;
-    const int col = (tr ? v_off<D>(row, cs) : k_off<D>(row, cs)) / 16 - row * (D / 8);  // XOR is self-inverse
-    const int rr = row < valid ? row : valid - 1;
-    lds_dma16(srcs[cp], (uint32_t)(rr * row_bytes + col * 16), dst + cp * (nrows * D * 2) + c * 1024);
-  }
-}
-
-// Transpose-read fragment (the A operand of a product whose contraction runs
-// over tile rows): rows `row` + {key0, key0 + 8} (+0..3 across lane groups),
-// columns 32 db + ..., exactly as the forward kernel gathers V^T.  `base` is
-// the tile address plus this lane's offset for column block db, formed once
-// per tile, so the row offsets are instruction immediates.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(uint32_t base, int row) {
-  const uint32_t va = base + row * (D * 2);  // base = tile + (vA ^ 64 db); rows become immediates
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)va);
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(va + 8 * D * 2));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// Per-lane base offset of tr_frag (lane 4t+s of 16-lane group g addresses row
-// t of a 4-row group, columns 4s..4s+3 of a 16-column slice).
-template <int D>
-__device__ __forceinline__ int tr_base(int lane) {
-  const int g4 = lane >> 4;
-  const int tr_t = (lane >> 2) & 3;
-  const int tr_s = lane & 3;
-  const int key0 = 4 * (g4 >> 1) + tr_t;
-  return v_off<D>(key0, 2 * (g4 & 1) + (tr_s >> 1)) + (tr_s & 1) * 8;
-}
 
 // Row of element i of a 32x32 MFMA result held by a lane in half hf.
 __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + (i & 3) + 4 * hf; }
@@ -204,27 +156,75 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
   const int64_t row_bytes = a.kv_ss * 2;
   const char* ksrc = (const char*)a.k + (b * a.kv_sb + h * a.kv_sh) * 2;
   const char* vsrc = (const char*)a.v + (b * a.kv_sb + h * a.kv_sh) * 2;
-  auto issue = [&](int t) {
+  // Copies: wave w takes the stage's 1 KiB chunks CPW w .. CPW w + CPW - 1
+  // (K tile, then V tile): one contiguous run, one M0.  Per-lane global
+  // offsets do not depend on the tile; the instruction offset is taken out.
+  static_assert(C::DQ_CPW == 4 || C::DQ_CPW == 2, "copies per wave");
+  constexpr int CPT = C::KT / 1024;  // chunks per tile
+  const int w_tile = (C::DQ_CPW * wave) / CPT;  // 0: K, 1: V
+  const char* w_src = w_tile == 0 ? ksrc : vsrc;
+  const uint32_t w_run = (uint32_t)(C::DQ_CPW * wave) * 1024;
+  uint32_t w_off[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < C::DQ_CPW; ++j) {
+    const int p = ((C::DQ_CPW * wave) % CPT + j) * 1024 + lane * 16;
+    const int rw = p / (D * 2);
+    const int pc = (p % (D * 2)) / 16;
+    const int lc = pc ^ (w_tile == 0 ? u_swz<D>(rw) : (k_off<D>(rw, pc) / 16 - rw * (D / 8)) ^ pc);
+    w_off[j] = (uint32_t)(rw * row_bytes + lc * 16) - 1024u * j;  // >= 0: chunk j's rows start at >= 1 KiB j
+  }
+  auto issue = [&](int t, uint32_t st) {
     const int64_t go = (int64_t)t * BKN * row_bytes;
-    const char* const srcs[3] = {ksrc + go, ksrc + go, vsrc + go};
-    copy_stage<D, 3, C::DQ_CPW>(srcs, 0b010, row_bytes, (int)(a.kv_len - (int64_t)t * BKN),
-                               base + (t % kStages) * C::DQ_STAGE, BKN, wave, lane);
+    const int valid = (int)(a.kv_len - (int64_t)t * BKN);
+    if (valid >= BKN) {
+      if constexpr (C::DQ_CPW == 4)
+        lds_dma_x4(w_src + go, w_off, st + w_run);
+      else
+        lds_dma_x2(w_src + go, w_off, st + w_run);
+      return;
+    }
+    // last, partial tile: keys past the block end re-read its last key
+#pragma unroll
+    for (int j = 0; j < C::DQ_CPW; ++j) {
+      const int p = ((C::DQ_CPW * wave) % CPT + j) * 1024 + lane * 16;
+      const int rw = p / (D * 2);
+      const int pc = (p % (D * 2)) / 16;
+      const int lc = pc ^ (w_tile == 0 ? u_swz<D>(rw) : (k_off<D>(rw, pc) / 16 - rw * (D / 8)) ^ pc);
+      const int rr = rw < valid ? rw : valid - 1;
+      lds_dma16(w_src + go, (uint32_t)(rr * row_bytes + lc * 16), st + w_run + j * 1024);
+    }
   };
-  const int vA = tr_base<D>(lane);
+  // per-lane LDS offsets: K rows (u_off) and V rows (k_off) for the row
+  // reads, row l32 (+32 an immediate), chunk 2 ks + hf; K^T transpose reads,
+  // rows key0 (lo) and key0 + 8 (hi) of each 16-row step, column block db by
+  // XOR with 64 db
+  int kro[C::KS], vro[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    kro[ks] = u_off<D>(l32, 2 * ks + hf);
+    vro[ks] = C::KT + k_off<D>(l32, 2 * ks + hf);
+  }
+  int tr_lo, tr_hi;
+  {
+    const int g4 = lane >> 4, tt = (lane >> 2) & 3, ss = lane & 3;
+    const int key0 = 4 * (g4 >> 1) + tt;
+    const int c0 = 2 * (g4 & 1) + (ss >> 1);
+    tr_lo = u_off<D>(key0, c0) + (ss & 1) * 8;
+    tr_hi = u_off<D>(key0 + 8, c0) + (ss & 1) * 8;
+  }
 
-  issue(0);
+  // stages rotate: tile t, t+1 (landed), t+2 (in flight)
+  uint32_t st_c = base, st_1 = base + C::DQ_STAGE, st_2 = base + 2 * C::DQ_STAGE;
+  issue(0, st_c);
   if (n_tiles > 1) {
-    issue(1);
+    issue(1, st_1);
     wait_vm<C::DQ_CPW>();
   } else {
     wait_vm<0>();
   }
   wg_barrier();
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + 2 < n_tiles) issue(t + 2);
-    const uint32_t kl = base + (t % kStages) * C::DQ_STAGE;
-    const uint32_t ktl = kl + C::KT;
-    const uint32_t vl = kl + 2 * C::KT;
+    if (t + 2 < n_tiles) issue(t + 2, st_2);
     const int kv_rel = clamp_i(klim - (int64_t)t * BKN, 0, BKN);  // visible keys of this tile: [0, kv_rel)
     const bool full = __all(kv_rel == BKN);  // wave-uniform
     bf16x2 dsp[16];
@@ -234,9 +234,10 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const int o = k_off<D>(l32 + 32 * kb, 2 * ks + hf);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(kl + o), qf[ks], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(vl + o), df[ks], dp, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(st_c + kro[ks] + kb * 32 * (D * 2)),
+                                                    qf[ks], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(st_c + vro[ks] + kb * 32 * (D * 2)),
+                                                     df[ks], dp, 0, 0, 0);
       }
       // dS^T = P^T (dP^T - delta), P^T = exp2(S^T c - LSE2), bf16 pairs;
       // no per-key test where every row of the wave sees the whole tile
@@ -267,23 +268,32 @@ __global__ __launch_bounds__(kBThreads) void bwd_dq_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);  // keep each half's operands short-lived (register budget)
     }
-    // dQ^T += K^T dS^T (bases formed per read: this kernel has no
-    // registers to hold four more per tile)
+    // dQ^T += K^T dS^T, K^T from the same K tile by transpose reads
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
         const bf16x8 pf = pack8(dsp, 8 * kb + 4 * tp);
+        const int row = 32 * kb + 16 * tp;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(ktl + (vA ^ (64 * db)), 32 * kb + 16 * tp), pf,
-                                                            acc[db], 0, 0, 0);
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(size_t)(st_c + ((uint32_t)tr_lo ^ (64u * db)) + row * (D * 2)));
+          const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_bf16x4*)(size_t)(st_c + ((uint32_t)tr_hi ^ (64u * db)) + row * (D * 2)));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            pf, acc[db], 0, 0, 0);
+        }
       }
     if (t + 2 < n_tiles)
       wait_vm<C::DQ_CPW>();  // tile t+1 landed; t+2 may still be in flight
     else
       wait_vm<0>();
     wg_barrier();
+    const uint32_t st_free = st_c;  // tile t's stage takes tile t+3
+    st_c = st_1;
+    st_1 = st_2;
+    st_2 = st_free;
   }
   if (!row_ok) return;
   float* dq = a.dq + (((int64_t)b * a.q_len + r) * a.heads + h) * D + 4 * hf;
@@ -425,8 +435,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
     // row being >= 128 bytes; the lead waves' extra 256 goes on the base)
     w_off[j] = (uint32_t)(rw * qrow_bytes + lc * 16) - 1024u * j;
   }
-  auto issue = [&](int t) {
-    const uint32_t st = stage(t);
+  auto issue = [&](int t, uint32_t st) {
     const int64_t row0 = (int64_t)t * BQK;
     const int64_t go = row0 * qrow_bytes;
     const int valid = (int)(a.q_len - row0);
@@ -475,40 +484,40 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
     tr_lo = u_off<D>(key0, c0) + (ss & 1) * 8;
     tr_hi = u_off<D>(key0 + 8, c0) + (ss & 1) * 8;
   }
-  auto tr_frag_u = [&](uint32_t tile, int db, int row) -> bf16x8 {
-    const uint32_t lo = tile + ((uint32_t)tr_lo ^ (64u * db)) + row * S::ROWB;
-    const uint32_t hi = tile + ((uint32_t)tr_hi ^ (64u * db)) + row * S::ROWB;
-    const bf16x4 vlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)lo);
-    const bf16x4 vhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)hi);
-    return __builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
   // P hand-over: this lane's 64 bytes as four 16-byte pieces, piece j at
   // 1 KiB j + 16 lane (consecutive lanes on consecutive banks)
   const uint32_t px_lane = base + S::PX_OFF + pair * S::PX_PAIR + lane * 16;
   typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_w;
   typedef __attribute__((address_space(3))) const f32x4 lds_f32x4;
 
-  issue(qt0);
+  // Stage addresses rotate by trip: the P side's tile t, the dS side's t-1
+  // and the copy target t+1 (which reuses t-2's stage).
+  uint32_t st_p = stage(qt0), st_n = stage(qt0 + 1), st_d = stage(qt0 + 2);
+  issue(qt0, st_p);
   wait_vm<0>();
   wg_barrier();
   const int n_iter = n_qt - qt0 + 1;  // the last trip serves only the dS side
   for (int i = 0; i < n_iter; ++i) {
     const int t = qt0 + i;
-    if (t + 1 < n_qt) issue(t + 1);
+    if (t + 1 < n_qt) issue(t + 1, st_n);
     const int tw = role == 0 ? t : t - 1;  // this wave's tile
     if (tw >= qt0 && tw < n_qt) {
-      const uint32_t st = stage(tw);
+      const uint32_t st = role == 0 ? st_p : st_d;
       const int64_t row_t0 = (int64_t)tw * BQK;
       const int lo = key_ok ? clamp_i(first_row - row_t0, 0, BQK) : BQK;  // rows [lo, hi) of the tile see the key
       const int hi = clamp_i(a.q_len - row_t0, 0, BQK);
-      // S = Q K^T (role 0) or dP = dO V^T (role 1), rows 0-31 and 32-63
+      // S = Q K^T (role 0) or dP = dO V^T (role 1), rows 0-31 and 32-63;
+      // per-lane bases once per tile, rows 32-63 an immediate
       f32x16 r0 = f32x16{}, r1 = f32x16{};
       const uint32_t rows = st + (role == 0 ? S::Q_OFF : S::DO_OFF);
+      uint32_t rb[C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) rb[ks] = rows + rofs[ks];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        r0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rows + rofs[ks]), fr[ks], r0, 0, 0, 0);
-        r1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rows + rofs[ks] + 32 * S::ROWB), fr[ks], r1,
-                                                     0, 0, 0);
+        r0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)rb[ks], fr[ks], r0, 0, 0, 0);
+        r1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(lds_bf16x8*)(size_t)(rb[ks] + 32 * S::ROWB), fr[ks], r1, 0, 0,
+                                                     0);
       }
       bf16x2 x[16];  // P (role 0) or dS (role 1) as bf16 pairs: rows of r0, then of r1
       if (role == 0) {
@@ -568,19 +577,36 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
           }
         }
       }
-      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1): four 16-row steps
+      // dV^T += dO^T P (role 0) or dK^T += Q^T dS (role 1): four 16-row
+      // steps; per-lane bases once per tile, the steps immediates
       const uint32_t trl = st + (role == 0 ? S::DO_OFF : S::Q_OFF);
+      uint32_t tb_lo[C::DB], tb_hi[C::DB];
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        tb_lo[db] = trl + ((uint32_t)tr_lo ^ (64u * db));
+        tb_hi[db] = trl + ((uint32_t)tr_hi ^ (64u * db));
+      }
 #pragma unroll
       for (int tp = 0; tp < 4; ++tp) {
         const bf16x8 xf = pack8(x, 4 * tp);
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag_u(trl, db, 16 * tp), xf, acc[db], 0, 0, 0);
+        for (int db = 0; db < C::DB; ++db) {
+          const bf16x4 vlo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(tb_lo[db] + 16 * tp * S::ROWB));
+          const bf16x4 vhi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(size_t)(tb_hi[db] + 16 * tp * S::ROWB));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(vlo, vhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            xf, acc[db], 0, 0, 0);
+        }
       }
     }
     wait_vm<0>();  // tile t+1 landed
     wait_lds();    // the P just written, before the other wave of the pair reads it
     wg_barrier();
+    const uint32_t st_free = st_d;  // tile t-1's stage takes tile t+2
+    st_d = st_p;
+    st_p = st_n;
+    st_n = st_free;
   }
   if (!key_ok) return;
   float* out = (role == 0 ? a.dv : a.dk) + (((int64_t)b * a.kv_cap + c) * a.heads + h) * D + 4 * hf;
