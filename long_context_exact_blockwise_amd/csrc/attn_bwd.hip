@@ -13,20 +13,21 @@
 //
 // Two kernels per block, eight waves per workgroup (two per SIMD, so one
 // wave's MFMAs overlap another's exponentials, LDS reads and barrier), each
-// streaming query or key tiles through an LDS ring of direct global->LDS
-// copies (the copy of tile t+2 is in flight while tile t is computed):
+// streaming query or key tiles through a three-stage LDS ring of direct
+// global->LDS copies:
 //   dq kernel:   a workgroup owns 256 query rows (32 per wave) and streams
-//                the block's 64-key tiles: S^T = K Q^T, dP^T = V dO^T, then
+//                the block's 64-key tiles (tile t+2 in flight while tile t
+//                is computed): S^T = K Q^T, dP^T = V dO^T, then
 //                dQ^T += K^T dS^T.  Q and dO fragments stay in registers.
 //   dkdv kernel: a workgroup owns 128 keys, 32 per pair of waves on one
-//                SIMD, and streams 32-row query tiles with their LSE and
-//                delta.  One wave of the pair holds K fragments, forms
-//                S = Q K^T and P, accumulates dV^T += dO^T P and hands P over
-//                through LDS; the other holds V fragments and, one tile
-//                behind, forms dP = dO V^T, dS = P (dP - delta) and
-//                accumulates dK^T += Q^T dS.  S and dP are formed here and
-//                again in the dq kernel: 14 D flops per visible pair against
-//                the 10 D of the five products.
+//                SIMD, and streams 64-row query tiles with their LSE and
+//                delta (tile t+1 in flight).  One wave of the pair holds K
+//                fragments, forms S = Q K^T and P for tile t, accumulates
+//                dV^T += dO^T P and hands P over through LDS; the other holds
+//                V fragments and, one tile behind, forms dP = dO V^T,
+//                dS = P (dP - delta) and accumulates dK^T += Q^T dS.  S and
+//                dP are formed here and again in the dq kernel: 14 D flops
+//                per visible pair against the 10 D of the five products.
 // Matrix products use v_mfma_f32_32x32x16_bf16 with the same operand layouts
 // as the forward kernel: transposed-operand fragments (K^T, dO^T, Q^T) come
 // from LDS with ds_read_b64_tr_b16 in the 4-row-group key order that matches
@@ -47,7 +48,6 @@ constexpr int kBWaves = 8;                 // waves per workgroup of the dq kern
 constexpr int kBThreads = 64 * kBWaves;
 constexpr int BQ = 32 * kBWaves;           // dq kernel: query rows per workgroup
 constexpr int BKN = 64;                    // dq kernel: keys per tile
-constexpr int BQT = 32;                    // dkdv kernel: query rows per tile
 constexpr int kStages = 3;                 // LDS ring depth of the dq kernel
 
 template <int D>
@@ -56,7 +56,6 @@ struct BCfg {
   static constexpr int DB = D / 32;
   static constexpr int ROWB = D * 2;
   static constexpr int KT = BKN * ROWB;        // bytes of a 64-key tile
-  static constexpr int QT = BQT * ROWB;        // bytes of a 32-row tile
   // dq stage: K (u_off placement: row reads for S, transpose reads for dQ),
   // V rows (row-read placement)
   static constexpr int DQ_STAGE = 2 * KT;
