@@ -1,5 +1,5 @@
 """Host checks of the build's job list: every source is compiled, the backward
-source as two objects (one kernel each) with its own scheduling flags, and the
+source as two objects (one kernel each) with its own scheduling strategy, and the
 scheduler flag that the fused kernel's traffic counters are tied to is part of
 the hash that bench.py checks."""
 
@@ -25,7 +25,9 @@ def test_backward_split_into_dq_and_dkdv_objects():
     assert set(bwd) == {"attn_bwd_dq", "attn_bwd_dkdv"}
     assert "-DRA_BWD_PART=1" in bwd["attn_bwd_dq"] and "-DRA_BWD_PART=2" in bwd["attn_bwd_dkdv"]
     ilp = "-amdgpu-sched-strategy=iterative-ilp"
+    max_ilp = "-amdgpu-sched-strategy=max-ilp"
     assert ilp not in bwd["attn_bwd_dq"] and ilp in bwd["attn_bwd_dkdv"]
+    assert max_ilp in bwd["attn_bwd_dq"] and max_ilp not in bwd["attn_bwd_dkdv"]
 
 
 def test_forward_flags_in_traffic_hash(monkeypatch):
