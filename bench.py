@@ -114,21 +114,35 @@ def read_traffic():
         return None
 
 
-def probe_peak(dev, iters: int = 200000, reps: int = 2) -> float:
+def probe_peak(dev, iters: int = 200000, reps: int = 2, random_operands: bool = False) -> float:
     """bf16 MFMA rate the part sustains under load (TFLOP/s): the library's
     MFMA-only probe on every CU (four 512-thread groups per CU, four waves per
-    SIMD, ~50 ms per launch), best of `reps`."""
+    SIMD, ~50 ms per launch), best of `reps`.  Its operands are a fixed
+    pattern of small values, or with `random_operands` seeded N(0, 1) bf16
+    values (more bits toggle per product: more power, a lower clock)."""
     import torch
     from long_context_exact_blockwise_amd import ringattn as ra
     wgs = 4 * 256
     out = torch.empty(wgs * ra.PROBE_THREADS, dtype=torch.float32, device=dev)
-    ra.ringattn_probe_mfma(out, wgs, 1000)
+    ops = None
+    if random_operands:
+        g = torch.Generator(device=dev)
+        g.manual_seed(0)
+        ops = torch.randn(wgs * ra.PROBE_THREADS * ra.PROBE_OPERANDS_PER_THREAD, generator=g, device=dev,
+                          dtype=torch.float32).to(torch.bfloat16)
+
+    def launch(n):
+        if ops is None:
+            ra.ringattn_probe_mfma(out, wgs, n)
+        else:
+            ra.ringattn_probe_mfma_data(ops, out, wgs, n)
+    launch(1000)
     torch.cuda.synchronize()
     best = 0.0
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        ra.ringattn_probe_mfma(out, wgs, iters)
+        launch(iters)
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
@@ -563,6 +577,7 @@ def main():
                                                   ms_step * 1e-3, args.steps)
 
     probed = probe_peak(dev) if wl.dtype == "bf16" else None
+    probed_rand = probe_peak(dev, iters=100000, random_operands=True) if wl.dtype == "bf16" else None
 
     if args.traffic_calib:
         n = 1 << 30
@@ -585,6 +600,11 @@ def main():
         "frac_of_probed": (achieved / probed) if probed else None,
         "probed_peak_note": "bf16 MFMA rate measured on this part under load by ringattn_probe_mfma "
                             "(MFMA-only kernel on every CU); peak is the published 2.5 PF figure",
+        "probed_peak_random_operands": probed_rand,
+        "frac_of_probed_random_operands": (achieved / probed_rand) if probed_rand else None,
+        "probed_peak_random_operands_note": "the same probe with seeded N(0, 1) bf16 operands "
+                                            "(ringattn_probe_mfma_data): the rate the part sustains on data like "
+                                            "the attention's, where power limits the clock",
     }
     if wl.dtype != "bf16":
         roofline.update(bound="latency", peak=None, frac=None)
@@ -622,10 +642,15 @@ def main():
         result["backward"] = backward_measure(x, wl, kb, vb, pos, o, lse, args.bwd_steps, 1, heads)
         if probed:
             result["backward"]["pct_of_probed_peak"] = 100.0 * result["backward"]["value"] / probed
+        if probed_rand:
+            result["backward"]["pct_of_probed_peak_random_operands"] = (100.0 * result["backward"]["value"] /
+                                                                        probed_rand)
     if not args.no_ffn:
         result["ffn"] = ffn_measure(dev, 10, 2)
         if probed:
             result["ffn"]["pct_of_probed_peak"] = 100.0 * result["ffn"]["value"] / probed
+        if probed_rand:
+            result["ffn"]["pct_of_probed_peak_random_operands"] = 100.0 * result["ffn"]["value"] / probed_rand
     if not args.no_workloads and args.workload == 3:
         # the timed workload's tensors are no longer needed
         del x, kb, vb, o, lse, ws

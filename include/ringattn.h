@@ -299,6 +299,17 @@ ra_status ringattn_probe_copy(const void* src, void* dst, int64_t bytes, hipStre
  * sustains under load. */
 ra_status ringattn_probe_mfma(float* out, int32_t workgroups, int32_t iters, hipStream_t stream);
 
+/* Measurement helper, not part of the attention path: the same probe with its
+ * operands read once per thread from `operands` (device memory, 16-byte
+ * aligned, workgroups * 512 * 32 bf16 values: four 8-element fragments per
+ * thread, thread-major) instead of a fixed pattern of small values.  With
+ * random bf16 operands, as the attention and feedforward products see, the
+ * part draws more power per product and holds a lower clock, so this gives
+ * the bf16 MFMA rate it sustains on such data.  Errors: RA_E_NULL, RA_E_SHAPE
+ * (the ranges of ringattn_probe_mfma), RA_E_ALIGN, RA_E_MEMTYPE. */
+ra_status ringattn_probe_mfma_data(const void* operands, float* out, int32_t workgroups, int32_t iters,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

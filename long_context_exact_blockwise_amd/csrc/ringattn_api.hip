@@ -758,7 +758,21 @@ ra_status ringattn_probe_mfma(float* out, int32_t workgroups, int32_t iters, hip
   if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 24))
     return fail(RA_E_SHAPE, "workgroups must be in [1, 65536] and iters in [1, 2^24]");
   if ((st = check_mem(out, false, "out")) != RA_OK) return st;
-  hipError_t e = ra::launch_probe_mfma(out, workgroups, iters, stream);
+  hipError_t e = ra::launch_probe_mfma(nullptr, out, workgroups, iters, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "probe launch");
+}
+
+ra_status ringattn_probe_mfma_data(const void* operands, float* out, int32_t workgroups, int32_t iters,
+                                   hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = need_ptr(operands, "operands")) != RA_OK) return st;
+  if ((st = need_ptr(out, "out")) != RA_OK) return st;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 24))
+    return fail(RA_E_SHAPE, "workgroups must be in [1, 65536] and iters in [1, 2^24]");
+  if ((st = check_mem(operands, false, "operands")) != RA_OK) return st;
+  if ((st = check_mem(out, false, "out")) != RA_OK) return st;
+  hipError_t e = ra::launch_probe_mfma(operands, out, workgroups, iters, stream);
   return e == hipSuccess ? RA_OK : hip_fail(e, "probe launch");
 }
 

@@ -30,7 +30,7 @@ SYMBOLS = (
     "ringattn_abi_version", "ringattn_status_str", "ringattn_last_error", "ringattn_ring_order",
     "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
     "ringattn_ring_fwd", "ringattn_probe_copy", "ringattn_bwd_delta", "ringattn_block_bwd", "ringattn_ring_bwd",
-    "ringattn_ffn_fwd", "ringattn_probe_mfma", "ringattn_ring_bwd_noalloc",
+    "ringattn_ffn_fwd", "ringattn_probe_mfma", "ringattn_ring_bwd_noalloc", "ringattn_probe_mfma_data",
 )
 NOALLOC_MAX_ROWS = 4 << 20
 
@@ -105,6 +105,8 @@ def load(path: str):
     L.ringattn_block_bwd.argtypes = [D, P, P, P, ctypes.c_int64, P, P, P, P, P, P, P]
     L.ringattn_probe_mfma.restype = ctypes.c_int
     L.ringattn_probe_mfma.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
+    L.ringattn_probe_mfma_data.restype = ctypes.c_int
+    L.ringattn_probe_mfma_data.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, P]
     L.ringattn_ffn_fwd.restype = ctypes.c_int
     L.ringattn_ffn_fwd.argtypes = [ctypes.POINTER(RaFfnDesc), P, P, P, P, P, P, P, P]
     L.ringattn_ring_bwd.restype = ctypes.c_int
@@ -227,6 +229,13 @@ PROBE_FLOP_PER_ITER_PER_WAVE = 4 * 32768  # four 32x32x16 products
 
 def ringattn_probe_mfma(out: torch.Tensor, workgroups: int, iters: int, stream=None):
     _check(lib().ringattn_probe_mfma(_ptr(out), workgroups, iters, _stream(stream)))
+
+
+PROBE_OPERANDS_PER_THREAD = 32  # bf16 values: four 8-element fragments
+
+
+def ringattn_probe_mfma_data(operands: torch.Tensor, out: torch.Tensor, workgroups: int, iters: int, stream=None):
+    _check(lib().ringattn_probe_mfma_data(_ptr(operands), _ptr(out), workgroups, iters, _stream(stream)))
 
 
 # ---- convenience wrappers (allocation of outputs / workspace with torch) ----

@@ -268,3 +268,12 @@ def test_probe_mfma_checks_before_enqueue():
     assert L.ringattn_probe_mfma(FAKE + 4, 1, 1, None) == ra.RA_E_ALIGN
     assert L.ringattn_probe_mfma(FAKE, 0, 1, None) == ra.RA_E_SHAPE
     assert L.ringattn_probe_mfma(FAKE, 1, 0, None) == ra.RA_E_SHAPE
+
+
+def test_probe_mfma_data_checks_before_enqueue():
+    L = ra.lib()
+    assert L.ringattn_probe_mfma_data(None, FAKE, 1, 1, None) == ra.RA_E_NULL
+    assert L.ringattn_probe_mfma_data(FAKE, None, 1, 1, None) == ra.RA_E_NULL
+    assert L.ringattn_probe_mfma_data(FAKE + 8, FAKE, 1, 1, None) == ra.RA_E_ALIGN
+    assert L.ringattn_probe_mfma_data(FAKE, FAKE, 0, 1, None) == ra.RA_E_SHAPE
+    assert L.ringattn_probe_mfma_data(FAKE, FAKE, 1, 1 << 25, None) == ra.RA_E_SHAPE
