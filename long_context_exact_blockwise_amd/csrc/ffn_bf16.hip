@@ -22,14 +22,11 @@
 namespace ra {
 namespace {
 
-// Rows of C per wave, in 32-row products: 2 gives eight waves, two per SIMD
-// (the default); 4 gives four waves of 128 x 128, one per SIMD, with half the
-// LDS operand traffic per product, which measured 9% slower.
-#ifndef RA_FFN_WM
-#define RA_FFN_WM 2
-#endif
+// Eight waves, two per SIMD, of 64 rows x 128 columns.  (Four waves of
+// 128 x 128, one per SIMD, with half the LDS operand traffic per product,
+// measured 9-15% slower: nothing covers a wave's barrier and copy issue.)
 constexpr int WTN = 4;                            // 32-column products per wave (128 columns)
-constexpr int WTM = RA_FFN_WM;                    // 32-row products per wave
+constexpr int WTM = 2;                            // 32-row products per wave (64 rows)
 constexpr int kGWaves = (256 / (32 * WTN)) * (256 / (32 * WTM));
 constexpr int kGThreads = 64 * kGWaves;
 constexpr int GBM = 256;                          // rows of C per workgroup
@@ -38,7 +35,7 @@ constexpr int GBK = 64;                           // contraction per stage
 constexpr int G_TILE = 256 * GBK * 2;             // 32 KiB: one operand tile (256 rows x 128 B)
 constexpr int G_STAGE = 2 * G_TILE;               // weights tile, then token tile
 constexpr int G_LDS = 2 * G_STAGE;                // two stages: 128 KiB
-constexpr int G_CPW = G_STAGE / 1024 / kGWaves;   // 1 KiB copies per wave per stage
+static_assert(G_STAGE / 1024 / kGWaves == 8, "two four-copy groups per wave and stage");
 
 // GELU, tanh form (Hendrycks and Gimpel): 0.5 x (1 + tanh(u)) with u =
 // sqrt(2/pi) (x + 0.044715 x^3), evaluated as x / (1 + e^(-2u)) (the same
@@ -88,33 +85,42 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
 
   const int64_t m0 = tm * GBM;
   const int n0 = tn * GBN;
-  const char* wsrc = (const char*)(g.b + (int64_t)n0 * g.ldb);
-  const char* xsrc = (const char*)(g.a + m0 * g.lda);
-  const int64_t wrow = g.ldb * 2, xrow = g.lda * 2;
-  const int wvalid = g.n - n0 < GBN ? g.n - n0 : GBN;
-  const int xvalid = (int)(g.m - m0 < GBM ? g.m - m0 : GBM);
   const uint32_t base = lds_addr_of(lds);
   const int nk = g.k / GBK;
 
-  // this wave's share of a stage: 64 copies of 1 KiB (8 rows x 128 B), the
-  // first 32 of the weight tile, the rest of the token tile; rows past the
-  // matrix edge re-read its last row (their products are never stored)
-  auto issue = [&](int kt) {
-    const uint32_t st = base + (kt & 1) * G_STAGE;
+  // Copies: a stage is 64 chunks of 1 KiB (8 rows x 128 B), chunks 0-31 the
+  // weight tile, 32-63 the token tile; wave w copies chunks 8w .. 8w + 7 as
+  // two four-copy groups, each under one M0.  Lane i of chunk q fills LDS
+  // bytes 16 i of it: row 8 q + i / 8, slot i % 8, which holds the global
+  // chunk the k_off placement puts there (its XOR is self-inverse).  Rows
+  // past the matrix edge re-read its last row (their products are never
+  // stored).  A group's instruction offsets add 1 KiB j to both addresses,
+  // so the lane offsets have 1 KiB j taken out; the source base sits 3 KiB
+  // before the tile's first row so that they stay non-negative when a
+  // clamped row is below 8 j (the addresses formed are the rows' own).
+  const bool cp_x = wave >= 4;
+  const char* csrc = (cp_x ? (const char*)(g.a + m0 * g.lda) : (const char*)(g.b + (int64_t)n0 * g.ldb)) - 3072;
+  uint32_t coff[2][4];
+  {
+    const int64_t rowb = (cp_x ? g.lda : g.ldb) * 2;
+    const int valid = cp_x ? (int)(g.m - m0 < GBM ? g.m - m0 : GBM) : (g.n - n0 < GBN ? g.n - n0 : GBN);
 #pragma unroll
-    for (int j = 0; j < G_CPW; ++j) {
-      const int gi = wave + kGWaves * j;
-      const int cp = gi >> 5;
-      const int c = gi & 31;
-      const int p = c * 1024 + lane * 16;
-      const int row = p >> 7;
-      const int cs = (p & 127) >> 4;
-      const int col = k_off<64>(row, cs) / 16 - row * 8;  // XOR is self-inverse
-      const int valid = cp ? xvalid : wvalid;
-      const int rr = row < valid ? row : valid - 1;
-      const char* src = (cp ? xsrc : wsrc) + kt * (GBK * 2);
-      lds_dma16(src, (uint32_t)(rr * (cp ? xrow : wrow) + col * 16), st + cp * G_TILE + c * 1024);
-    }
+    for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int q = 8 * (wave & 3) + 4 * gq + j;
+        const int row = 8 * q + (lane >> 3);
+        const int col = k_off<64>(row, lane & 7) / 16 - row * 8;
+        const int rr = row < valid ? row : valid - 1;
+        coff[gq][j] = (uint32_t)(rr * rowb + col * 16 + 3072 - 1024 * j);
+      }
+  }
+  const uint32_t cdst = (cp_x ? G_TILE : 0) + 8192 * (wave & 3);
+  auto issue = [&](int kt, int stage) {
+    const char* src = csrc + kt * (GBK * 2);
+    const uint32_t st = base + stage * G_STAGE + cdst;
+    lds_dma_x4(src, coff[0], st);
+    lds_dma_x4(src, coff[1], st + 4096);
   };
 
   f32x16 acc[WTN][WTM];
@@ -123,29 +129,30 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
 #pragma unroll
     for (int mi = 0; mi < WTM; ++mi) acc[ni][mi] = f32x16{};
 
-  // per-lane byte offsets of this wave's operand rows for k-step ks (first
-  // 32-row group; each further group is 4 KiB on, an instruction immediate:
-  // the chunk XOR of k_off depends on the row only through bits 1..3)
-  uint32_t aoff[GBK / 16], boff[GBK / 16];
+  // per-lane LDS addresses of this wave's operand rows for stage s and
+  // k-step ks (first 32-row group; each further group is 4 KiB on, an
+  // instruction immediate: the chunk XOR of k_off depends on the row only
+  // through bits 1..3), formed once
+  uint32_t aad[2][GBK / 16], bad[2][GBK / 16];
 #pragma unroll
-  for (int ks = 0; ks < GBK / 16; ++ks) {
-    aoff[ks] = (uint32_t)k_off<64>(wn * 128 + l32, 2 * ks + hf);
-    boff[ks] = (uint32_t)(G_TILE + k_off<64>(wm * 32 * WTM + l32, 2 * ks + hf));
-  }
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      aad[st][ks] = base + st * G_STAGE + (uint32_t)k_off<64>(wn * 128 + l32, 2 * ks + hf);
+      bad[st][ks] = base + st * G_STAGE + (uint32_t)(G_TILE + k_off<64>(wm * 32 * WTM + l32, 2 * ks + hf));
+    }
 
-  issue(0);
-  wait_vm<0>();
-  wg_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) issue(kt + 1);
-    const uint32_t sb = base + (kt & 1) * G_STAGE;
+  // one k-tile from stage `stage` (a literal at both call sites), with the
+  // copy of the next k-tile into the other stage in flight
+  auto ktile = [&](int kt, int stage) {
+    if (kt + 1 < nk) issue(kt + 1, stage ^ 1);
     // operands of k-step ks+1 are read while the products of k-step ks run
     bf16x8 af[2][WTN], bfr[2][WTM];
     auto load = [&](int buf, int ks) {
 #pragma unroll
-      for (int ni = 0; ni < WTN; ++ni) af[buf][ni] = *(lds_bf16x8*)(size_t)(sb + aoff[ks] + ni * 4096);
+      for (int ni = 0; ni < WTN; ++ni) af[buf][ni] = *(lds_bf16x8*)(size_t)(aad[stage][ks] + ni * 4096);
 #pragma unroll
-      for (int mi = 0; mi < WTM; ++mi) bfr[buf][mi] = *(lds_bf16x8*)(size_t)(sb + boff[ks] + mi * 4096);
+      for (int mi = 0; mi < WTM; ++mi) bfr[buf][mi] = *(lds_bf16x8*)(size_t)(bad[stage][ks] + mi * 4096);
     };
     load(0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -163,6 +170,14 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
     }
     wait_vm<0>();
     wg_barrier();
+  };
+
+  issue(0, 0);
+  wait_vm<0>();
+  wg_barrier();
+  for (int kt = 0; kt < nk; kt += 2) {
+    ktile(kt, 0);
+    if (kt + 1 < nk) ktile(kt + 1, 1);
   }
 
   // epilogue: element i of acc[ni][mi] is column n0 + 128 wn + 32 ni +
