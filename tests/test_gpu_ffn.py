@@ -95,3 +95,21 @@ def test_full_size_sampled_rows():
     idx = torch.as_tensor(rows, device=x.device)
     ref = oracle.blockwise_ffn(_f64(x.index_select(0, idx)), _f64(w1), _f64(b1), _f64(w2), _f64(b2))
     print(_check(y.index_select(0, idx), ref, f"{wl.name}, {len(rows)} sampled rows"))
+
+
+def test_persistent_walk_with_ragged_edges():
+    """More tiles than workgroups, so every workgroup walks several tiles and
+    prefetches the next one beside its epilogue, with a ragged last row tile
+    (77 rows) and a ragged last column tile in both layers (d_ff = 1088,
+    d = 320): sampled rows of every row tile, including the ragged one,
+    against the oracle; every output scanned for NaN/Inf."""
+    rows, d, f = 256 * 300 + 77, 320, 1088
+    x, w1, b1, w2, b2 = inputs.make_ffn_inputs(rows, d, f, cuda(), seed=11)
+    y = ra.ffn_forward(x, w1, b1, w2, b2, block_rows=0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    tiles = range(0, rows, 256)
+    pick = sorted({min(t + o, rows - 1) for t in tiles[::7] for o in (0, 131, 255)} | {rows - 77, rows - 1})
+    idx = torch.as_tensor(pick, device=x.device)
+    ref = oracle.blockwise_ffn(_f64(x.index_select(0, idx)), _f64(w1), _f64(b1), _f64(w2), _f64(b2))
+    print(_check(y.index_select(0, idx), ref, f"rows {rows} d {d} f {f}, {len(pick)} sampled rows"))
