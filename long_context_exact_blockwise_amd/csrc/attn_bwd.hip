@@ -525,28 +525,41 @@ __global__ __launch_bounds__(kBThreads) void bwd_dkdv_kernel(BwdArgs a) {
         // needed, and exp2(-|x|) covers rows without a visible key: x =
         // S c - LSE2 <= 0 for a row's visible keys (LSE is at least each
         // visible score), while LSE = -inf makes x = +inf and P = 0.
+        // (the branch is taken once for the whole tile, so that the common
+        // path is one straight block the scheduler can interleave)
         const bool full = hi == BQK && __all(lo == 0);
+        if (full) {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const f32x16& r = h2 == 0 ? r0 : r1;
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x16& r = h2 == 0 ? r0 : r1;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (32 * h2 + 8 * g + 4 * hf) * 4);
-            float v[4];
-            if (full) {
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (32 * h2 + 8 * g + 4 * hf) * 4);
+              float v[4];
 #pragma unroll
               for (int j = 0; j < 4; ++j)
                 v[j] = __builtin_amdgcn_exp2f(-__builtin_fabsf(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)));
-            } else {
+              x[8 * h2 + 2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+              x[8 * h2 + 2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
+            }
+          }
+        } else {
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x16& r = h2 == 0 ? r0 : r1;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 l4 = *(lds_f32x4*)(size_t)(st + S::LSE_OFF + (32 * h2 + 8 * g + 4 * hf) * 4);
+              float v[4];
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int row = 32 * h2 + acc_row(4 * g + j, hf);
                 const bool vis = row >= lo && row < hi && l4[j] > -INFINITY;
                 v[j] = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(r[4 * g + j], c2, -l4[j] * kLog2e)) : 0.f;
               }
+              x[8 * h2 + 2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
+              x[8 * h2 + 2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
             }
-            x[8 * h2 + 2 * g] = bf16x2{(__bf16)v[0], (__bf16)v[1]};
-            x[8 * h2 + 2 * g + 1] = bf16x2{(__bf16)v[2], (__bf16)v[3]};
           }
         }
         const uint32_t px = px_lane + (i & 1) * S::PX_BYTES;
