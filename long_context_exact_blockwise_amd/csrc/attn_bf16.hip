@@ -144,7 +144,11 @@ __device__ __forceinline__ float softmax_redo(const f32x16 (&s)[2], float c2, fl
 // instruction offset moves the LDS destination and the global address alike,
 // so lane offsets are passed with that offset taken out (ko_j = K offset -
 // 1 KiB j) and the V base is passed 1 KiB DPW low.  Changing M0 while copies
-// are in flight stalls the wave, so it is set once per slot.
+// are in flight stalls the wave, so it is set once per slot.  The loads start
+// after `s_nop 4`: five wait states between a VALU write of an SGPR (the
+// bases come from v_readfirstlane; spilled SGPRs return by v_readlane) and a
+// VMEM instruction reading it, which the compiler does not insert inside
+// inline assembly.
 template <int DPW>
 __device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbase, const uint32_t (&ko)[DPW],
                                              const uint32_t (&vo)[DPW], uint32_t m0) {
@@ -161,7 +165,7 @@ __device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbas
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %5\n\t"
-        "s_nop 0\n\t"
+        "s_nop 4\n\t"
         "global_load_lds_dwordx4 %1, %6\n\t"
         "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
         "global_load_lds_dwordx4 %3, %7 offset:2048\n\t"
@@ -176,7 +180,7 @@ __device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbas
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
+        "s_nop 4\n\t"
         "global_load_lds_dwordx4 %1, %4\n\t"
         "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
         "s_mov_b32 m0, %0"

@@ -68,6 +68,12 @@ __device__ __forceinline__ float pair_sum(float x) {
 // flight before the next LDS read of any buffer, which serialises the prefetch
 // with the compute.  The kernel waits for its copies itself (s_waitcnt
 // vmcnt) before the barrier that publishes a buffer.
+// Every block starts its loads after `s_nop 4`: a VMEM instruction may read
+// an SGPR only five wait states after a VALU instruction wrote it (the base
+// comes from v_readfirstlane, and a spilled SGPR is restored by v_readlane),
+// and the compiler inserts no wait states for instructions inside inline
+// assembly.  Without them the copy can take a stale base address.  The same
+// wait also covers the one wait state after M0 is written.
 __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
   // (readfirstlane returns int: widen through uint32_t, never by sign extension)
   const uint64_t bv = (uint64_t)base;
@@ -78,7 +84,7 @@ __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint3
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -97,7 +103,7 @@ __device__ __forceinline__ void lds_dma4(const char* base, uint32_t voff, uint32
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dword %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -119,7 +125,7 @@ __device__ __forceinline__ void lds_dma_x4(const char* base, const uint32_t (&of
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %5\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dwordx4 %1, %6\n\t"
       "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
       "global_load_lds_dwordx4 %3, %6 offset:2048\n\t"
@@ -145,7 +151,7 @@ __device__ __forceinline__ void lds_dma_1x4(const char* dbase, uint32_t doff, co
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %6\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dword %5, %7\n\t"
       "global_load_lds_dwordx4 %1, %8 offset:256\n\t"
       "global_load_lds_dwordx4 %2, %8 offset:1280\n\t"
@@ -167,7 +173,7 @@ __device__ __forceinline__ void lds_dma_x2(const char* base, const uint32_t (&of
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dwordx4 %1, %4\n\t"
       "global_load_lds_dwordx4 %2, %4 offset:1024\n\t"
       "s_mov_b32 m0, %0"
@@ -187,7 +193,7 @@ __device__ __forceinline__ void lds_dma_1x2(const char* dbase, uint32_t doff, co
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %4\n\t"
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "global_load_lds_dword %3, %5\n\t"
       "global_load_lds_dwordx4 %1, %6 offset:256\n\t"
       "global_load_lds_dwordx4 %2, %6 offset:1280\n\t"
