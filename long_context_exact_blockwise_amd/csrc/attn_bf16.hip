@@ -144,11 +144,12 @@ __device__ __forceinline__ float softmax_redo(const f32x16 (&s)[2], float c2, fl
 // instruction offset moves the LDS destination and the global address alike,
 // so lane offsets are passed with that offset taken out (ko_j = K offset -
 // 1 KiB j) and the V base is passed 1 KiB DPW low.  Changing M0 while copies
-// are in flight stalls the wave, so it is set once per slot.  The loads start
-// after `s_nop 4`: five wait states between a VALU write of an SGPR (the
-// bases come from v_readfirstlane; spilled SGPRs return by v_readlane) and a
-// VMEM instruction reading it, which the compiler does not insert inside
-// inline assembly.
+// are in flight stalls the wave, so it is set once per slot.  The loads read
+// the bases from copies made by s_mov_b64 inside the block: an SGPR written
+// by a VALU instruction (v_readfirstlane here, v_readlane for a spilled SGPR)
+// may be read by a VMEM instruction only five wait states later, which the
+// compiler does not insert inside inline assembly; one written by a scalar
+// instruction needs none.
 template <int DPW>
 __device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbase, const uint32_t (&ko)[DPW],
                                              const uint32_t (&vo)[DPW], uint32_t m0) {
@@ -161,31 +162,35 @@ __device__ __forceinline__ void lds_dma_slot(const char* kbase, const char* vbas
   const uint64_t kbs = ((uint64_t)khi << 32) | klo;
   const uint64_t vbs = ((uint64_t)vhi << 32) | vlo;
   uint32_t saved;
+  uint64_t tk, tv;
   if constexpr (DPW == 2) {
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %5\n\t"
-        "s_nop 4\n\t"
-        "global_load_lds_dwordx4 %1, %6\n\t"
-        "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
-        "global_load_lds_dwordx4 %3, %7 offset:2048\n\t"
-        "global_load_lds_dwordx4 %4, %7 offset:3072\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(ko[0]), "v"(ko[1]), "v"(vo[0]), "v"(vo[1]), "s"(__builtin_amdgcn_readfirstlane(m0)), "s"(kbs),
-          "s"(vbs)
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[m0]\n\t"
+        "s_mov_b64 %[tk], %[kb]\n\t"
+        "s_mov_b64 %[tv], %[vb]\n\t"
+        "global_load_lds_dwordx4 %[k0], %[tk]\n\t"
+        "global_load_lds_dwordx4 %[k1], %[tk] offset:1024\n\t"
+        "global_load_lds_dwordx4 %[v0], %[tv] offset:2048\n\t"
+        "global_load_lds_dwordx4 %[v1], %[tv] offset:3072\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved), [tk] "=&s"(tk), [tv] "=&s"(tv)
+        : [k0] "v"(ko[0]), [k1] "v"(ko[1]), [v0] "v"(vo[0]), [v1] "v"(vo[1]),
+          [m0] "s"(__builtin_amdgcn_readfirstlane(m0)), [kb] "s"(kbs), [vb] "s"(vbs)
         : "memory");
   } else {
     static_assert(DPW == 1, "one or two chunks per wave");
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 4\n\t"
-        "global_load_lds_dwordx4 %1, %4\n\t"
-        "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(ko[0]), "v"(vo[0]), "s"(__builtin_amdgcn_readfirstlane(m0)), "s"(kbs), "s"(vbs)
+        "s_mov_b32 %[sv], m0\n\t"
+        "s_mov_b32 m0, %[m0]\n\t"
+        "s_mov_b64 %[tk], %[kb]\n\t"
+        "s_mov_b64 %[tv], %[vb]\n\t"
+        "global_load_lds_dwordx4 %[k0], %[tk]\n\t"
+        "global_load_lds_dwordx4 %[v0], %[tv] offset:1024\n\t"
+        "s_mov_b32 m0, %[sv]"
+        : [sv] "=&s"(saved), [tk] "=&s"(tk), [tv] "=&s"(tv)
+        : [k0] "v"(ko[0]), [v0] "v"(vo[0]), [m0] "s"(__builtin_amdgcn_readfirstlane(m0)), [kb] "s"(kbs),
+          [vb] "s"(vbs)
         : "memory");
   }
 }

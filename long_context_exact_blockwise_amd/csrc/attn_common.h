@@ -68,46 +68,50 @@ __device__ __forceinline__ float pair_sum(float x) {
 // flight before the next LDS read of any buffer, which serialises the prefetch
 // with the compute.  The kernel waits for its copies itself (s_waitcnt
 // vmcnt) before the barrier that publishes a buffer.
-// Every block starts its loads after `s_nop 4`: a VMEM instruction may read
-// an SGPR only five wait states after a VALU instruction wrote it (the base
-// comes from v_readfirstlane, and a spilled SGPR is restored by v_readlane),
-// and the compiler inserts no wait states for instructions inside inline
-// assembly.  Without them the copy can take a stale base address.  The same
-// wait also covers the one wait state after M0 is written.
-__device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
-  // (readfirstlane returns int: widen through uint32_t, never by sign extension)
-  const uint64_t bv = (uint64_t)base;
+// Every block rewrites its base SGPRs with a scalar self-copy (s_mov_b64 s,
+// s) before the loads: a VMEM instruction may read an SGPR only five wait
+// states after a VALU instruction wrote it (the base comes from
+// v_readfirstlane, and a spilled SGPR is restored by v_readlane), the
+// compiler inserts no wait states for instructions inside inline assembly,
+// and an SGPR last written by a scalar instruction needs none.  Without it
+// the load can take a stale base address.  The copy also gives the one wait
+// state a load needs after M0 is written.
+// A wave-uniform pointer as a 64-bit scalar value (readfirstlane returns
+// int: widen through uint32_t, never by sign extension).
+__device__ __forceinline__ uint64_t sbase(const char* p) {
+  const uint64_t bv = (uint64_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  return ((uint64_t)hi << 32) | lo;
+}
+// 16 bytes per lane (global_load_lds_dwordx4) from base + voff.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
+  uint64_t bs = sbase(base);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_mov_b64 %[bs], %[bs]\n\t"
+      "global_load_lds_dwordx4 %[o0], %[bs]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved), [bs] "+s"(bs)
+      : [o0] "v"(voff), [m0] "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 
 // The same for 4 bytes per lane (global_load_lds_dword): lane i's dword lands
 // at LDS byte lds_addr + 4 i.
 __device__ __forceinline__ void lds_dma4(const char* base, uint32_t voff, uint32_t lds_addr) {
-  const uint64_t bv = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint64_t bs = sbase(base);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dword %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(bs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_mov_b64 %[bs], %[bs]\n\t"
+      "global_load_lds_dword %[o0], %[bs]\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved), [bs] "+s"(bs)
+      : [o0] "v"(voff), [m0] "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 
@@ -117,22 +121,20 @@ __device__ __forceinline__ void lds_dma4(const char* base, uint32_t voff, uint32
 // off[j] is the lane's global offset with 1 KiB j taken out).  base and
 // lds_addr are wave-uniform.
 __device__ __forceinline__ void lds_dma_x4(const char* base, const uint32_t (&off)[4], uint32_t lds_addr) {
-  const uint64_t bv = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint64_t bs = sbase(base);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %5\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %6\n\t"
-      "global_load_lds_dwordx4 %2, %6 offset:1024\n\t"
-      "global_load_lds_dwordx4 %3, %6 offset:2048\n\t"
-      "global_load_lds_dwordx4 %4, %6 offset:3072\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(bs)
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_mov_b64 %[bs], %[bs]\n\t"
+      "global_load_lds_dwordx4 %[o0], %[bs]\n\t"
+      "global_load_lds_dwordx4 %[o1], %[bs] offset:1024\n\t"
+      "global_load_lds_dwordx4 %[o2], %[bs] offset:2048\n\t"
+      "global_load_lds_dwordx4 %[o3], %[bs] offset:3072\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved), [bs] "+s"(bs)
+      : [o0] "v"(off[0]), [o1] "v"(off[1]), [o2] "v"(off[2]), [o3] "v"(off[3]),
+        [m0] "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 
@@ -141,65 +143,54 @@ __device__ __forceinline__ void lds_dma_x4(const char* base, const uint32_t (&of
 // lds_addr + 256 + 1 KiB j from base + off[j] + 256 + 1 KiB j.
 __device__ __forceinline__ void lds_dma_1x4(const char* dbase, uint32_t doff, const char* base, const uint32_t (&off)[4],
                                             uint32_t lds_addr) {
-  const uint64_t dv = (uint64_t)dbase, bv = (uint64_t)base;
-  const uint32_t dlo = __builtin_amdgcn_readfirstlane((uint32_t)dv);
-  const uint32_t dhi = __builtin_amdgcn_readfirstlane((uint32_t)(dv >> 32));
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t ds = ((uint64_t)dhi << 32) | dlo, bs = ((uint64_t)hi << 32) | lo;
+  uint64_t ds = sbase(dbase), bs = sbase(base);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %6\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dword %5, %7\n\t"
-      "global_load_lds_dwordx4 %1, %8 offset:256\n\t"
-      "global_load_lds_dwordx4 %2, %8 offset:1280\n\t"
-      "global_load_lds_dwordx4 %3, %8 offset:2304\n\t"
-      "global_load_lds_dwordx4 %4, %8 offset:3328\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(doff), "s"(__builtin_amdgcn_readfirstlane(lds_addr)),
-        "s"(ds), "s"(bs)
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_mov_b64 %[ds], %[ds]\n\t"
+      "s_mov_b64 %[bs], %[bs]\n\t"
+      "global_load_lds_dword %[od], %[ds]\n\t"
+      "global_load_lds_dwordx4 %[o0], %[bs] offset:256\n\t"
+      "global_load_lds_dwordx4 %[o1], %[bs] offset:1280\n\t"
+      "global_load_lds_dwordx4 %[o2], %[bs] offset:2304\n\t"
+      "global_load_lds_dwordx4 %[o3], %[bs] offset:3328\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved), [ds] "+s"(ds), [bs] "+s"(bs)
+      : [o0] "v"(off[0]), [o1] "v"(off[1]), [o2] "v"(off[2]), [o3] "v"(off[3]), [od] "v"(doff),
+        [m0] "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 // Two-copy forms (D = 64: two 1 KiB chunks per wave).
 __device__ __forceinline__ void lds_dma_x2(const char* base, const uint32_t (&off)[4], uint32_t lds_addr) {
-  const uint64_t bv = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t bs = ((uint64_t)hi << 32) | lo;
+  uint64_t bs = sbase(base);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %4\n\t"
-      "global_load_lds_dwordx4 %2, %4 offset:1024\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off[0]), "v"(off[1]), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(bs)
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_mov_b64 %[bs], %[bs]\n\t"
+      "global_load_lds_dwordx4 %[o0], %[bs]\n\t"
+      "global_load_lds_dwordx4 %[o1], %[bs] offset:1024\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved), [bs] "+s"(bs)
+      : [o0] "v"(off[0]), [o1] "v"(off[1]), [m0] "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 __device__ __forceinline__ void lds_dma_1x2(const char* dbase, uint32_t doff, const char* base, const uint32_t (&off)[4],
                                             uint32_t lds_addr) {
-  const uint64_t dv = (uint64_t)dbase, bv = (uint64_t)base;
-  const uint32_t dlo = __builtin_amdgcn_readfirstlane((uint32_t)dv);
-  const uint32_t dhi = __builtin_amdgcn_readfirstlane((uint32_t)(dv >> 32));
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)bv);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
-  const uint64_t ds = ((uint64_t)dhi << 32) | dlo, bs = ((uint64_t)hi << 32) | lo;
+  uint64_t ds = sbase(dbase), bs = sbase(base);
   uint32_t saved;
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %4\n\t"
-      "s_nop 4\n\t"
-      "global_load_lds_dword %3, %5\n\t"
-      "global_load_lds_dwordx4 %1, %6 offset:256\n\t"
-      "global_load_lds_dwordx4 %2, %6 offset:1280\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(off[0]), "v"(off[1]), "v"(doff), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(ds), "s"(bs)
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[m0]\n\t"
+      "s_mov_b64 %[ds], %[ds]\n\t"
+      "s_mov_b64 %[bs], %[bs]\n\t"
+      "global_load_lds_dword %[od], %[ds]\n\t"
+      "global_load_lds_dwordx4 %[o0], %[bs] offset:256\n\t"
+      "global_load_lds_dwordx4 %[o1], %[bs] offset:1280\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved), [ds] "+s"(ds), [bs] "+s"(bs)
+      : [o0] "v"(off[0]), [o1] "v"(off[1]), [od] "v"(doff), [m0] "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 

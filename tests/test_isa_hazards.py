@@ -5,10 +5,12 @@ A VMEM instruction may read an SGPR only five wait states after a VALU
 instruction wrote it (v_readfirstlane forming a copy's base address, or
 v_readlane restoring a spilled SGPR).  The compiler inserts these wait states
 for the instructions it generates but not for instructions inside inline
-assembly, so every copy block starts with `s_nop 4`.  This test disassembles
+assembly, so every copy block either starts with `s_nop 4` or first copies
+its bases with s_mov_b64 (a scalar write needs no wait states before a VMEM
+read).  This test disassembles
 the code objects of both built libraries and looks, before every
 global_load_lds, for a VALU write of its base SGPRs fewer than five wait
-states back in program order.
+states back in program order that no scalar write of them follows.
 """
 import os
 import re
@@ -52,6 +54,18 @@ def _sgprs_written_by_valu(ins):
     return set()
 
 
+_SALU_DST = re.compile(r"^s_(?!cmp|bitcmp|waitcnt|nop|barrier|branch|cbranch|setprio|sleep|sendmsg|endpgm|setpc|swappc|getpc)\w+\s+s(?:\[(\d+):(\d+)\]|(\d+)\b)")
+
+
+def _sgprs_written_by_salu(ins):
+    m = _SALU_DST.match(ins)
+    if not m:
+        return set()
+    if m.group(3) is not None:
+        return {int(m.group(3))}
+    return set(range(int(m.group(1)), int(m.group(2)) + 1))
+
+
 def _wait_states(ins):
     m = re.match(r"^s_nop\s+(?:0x)?([0-9a-f]+)", ins)
     if m:
@@ -68,10 +82,11 @@ def find_hazards(text):
             continue
         need = set(range(int(m.group(1)), int(m.group(2)) + 1))
         states, j = 0, i - 1
-        while j >= 0 and states < 5 and seq[j][1] == fn:
+        while j >= 0 and states < 5 and seq[j][1] == fn and need:
             if _sgprs_written_by_valu(seq[j][0]) & need:
                 found.append((fn, seq[j][0], ins, states))
                 break
+            need -= _sgprs_written_by_salu(seq[j][0])  # rewritten by a scalar instruction: no wait needed
             states += _wait_states(seq[j][0])
             j -= 1
     return found
@@ -107,6 +122,9 @@ def test_checker_flags_a_close_valu_write():
     assert len(find_hazards(text)) == 1
     assert find_hazards(text.replace("s_nop 0 ", "s_nop 4 ")) == []
     assert find_hazards(text.replace("v_readlane_b32 s19", "v_readlane_b32 s21")) == []
+    # a scalar copy of the base between the two needs no wait states
+    bridged = text.replace("\ts_nop 0 ", "\ts_mov_b64 s[18:19], s[40:41] ")
+    assert "s_mov_b64 s[18:19]" in bridged and find_hazards(bridged) == []
 
 
 @pytest.mark.parametrize("lib", [B.OUT, B.CHECK_OUT], ids=["library", "checking_library"])
