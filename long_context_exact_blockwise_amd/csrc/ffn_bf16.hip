@@ -38,6 +38,7 @@ constexpr int G_TILE = 256 * GBK * 2;             // 32 KiB: one operand tile (2
 constexpr int G_STAGE = 2 * G_TILE;               // weights tile, then token tile
 constexpr int G_LDS = 2 * G_STAGE;                // two stages: 128 KiB
 static_assert(G_STAGE / 1024 / kGWaves == 8, "two four-copy groups per wave and stage");
+static_assert((GBK / 16) % 2 == 0, "a k-tile ends on operand buffer 1, so the next one starts on buffer 0");
 
 // GELU, tanh form (Hendrycks and Gimpel): 0.5 x (1 + tanh(u)) with u =
 // sqrt(2/pi) (x + 0.044715 x^3), evaluated as x / (1 + e^(-2u)) (the same
@@ -160,27 +161,39 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
     for (int ni = 0; ni < WTN; ++ni)
 #pragma unroll
       for (int mi = 0; mi < WTM; ++mi) acc[ni][mi] = f32x16{};
+    // operand buffers of two k-steps: k-step ks+1's are read while k-step
+    // ks's products run
+    bf16x8 af[2][WTN], bfr[2][WTM];
+    auto load = [&](int buf, int stage, int ks) {
+#pragma unroll
+      for (int ni = 0; ni < WTN; ++ni) af[buf][ni] = *(lds_bf16x8*)(size_t)(aad[stage][ks] + ni * 4096);
+#pragma unroll
+      for (int mi = 0; mi < WTM; ++mi) bfr[buf][mi] = *(lds_bf16x8*)(size_t)(bad[stage][ks] + mi * 4096);
+    };
     wait_vm<0>();  // this tile's first k-tile landed
     wg_barrier();
+    load(0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // one k-tile from stage `stage` (a literal at both call sites), with the
-    // copy of the next k-tile into the other stage in flight
+    // copy of the next k-tile into the other stage in flight.  Its first
+    // operands are in buffer 0 on entry.  After the last k-step's operands
+    // are read, the wave waits for its reads and copies and meets the others
+    // at the barrier (every read of this stage done, the next stage landed),
+    // then reads the next k-tile's first operands under the last k-step's
+    // products.
     auto ktile = [&](int kt, int stage) {
       if (kt + 1 < nk) issue(cur, kt + 1, stage ^ 1);
-      // operands of k-step ks+1 are read while the products of k-step ks run
-      bf16x8 af[2][WTN], bfr[2][WTM];
-      auto load = [&](int buf, int ks) {
-#pragma unroll
-        for (int ni = 0; ni < WTN; ++ni) af[buf][ni] = *(lds_bf16x8*)(size_t)(aad[stage][ks] + ni * 4096);
-#pragma unroll
-        for (int mi = 0; mi < WTM; ++mi) bfr[buf][mi] = *(lds_bf16x8*)(size_t)(bad[stage][ks] + mi * 4096);
-      };
-      load(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < GBK / 16; ++ks) {
         const int cb = ks & 1;
-        if (ks + 1 < GBK / 16) load(cb ^ 1, ks + 1);  // issued before this step's products
+        if (ks + 1 < GBK / 16) {
+          load(cb ^ 1, stage, ks + 1);  // issued before this step's products
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+          wg_barrier();
+          if (kt + 1 < nk) load(cb ^ 1, stage ^ 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ni = 0; ni < WTN; ++ni)
@@ -189,8 +202,6 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
             acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cb][ni], bfr[cb][mi], acc[ni][mi], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      wait_vm<0>();
-      wg_barrier();
     };
     for (int kt = 0; kt < nk; kt += 2) {
       ktile(kt, 0);
