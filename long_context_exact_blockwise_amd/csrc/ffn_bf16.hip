@@ -36,7 +36,8 @@ constexpr int GBN = 256;                          // columns of C per workgroup
 constexpr int GBK = 64;                           // contraction per stage
 constexpr int G_TILE = 256 * GBK * 2;             // 32 KiB: one operand tile (256 rows x 128 B)
 constexpr int G_STAGE = 2 * G_TILE;               // weights tile, then token tile
-constexpr int G_LDS = 2 * G_STAGE;                // two stages: 128 KiB
+constexpr int G_BIAS = 2 * G_STAGE;               // two 512-byte bias slices (tile parity) after the stages
+constexpr int G_LDS = G_BIAS + 2 * GBN * 2;        // 129 KiB
 static_assert(G_STAGE / 1024 / kGWaves == 8, "two four-copy groups per wave and stage");
 static_assert((GBK / 16) % 2 == 0, "a k-tile ends on operand buffer 1, so the next one starts on buffer 0");
 
@@ -149,12 +150,28 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
       bad[st][ks] = base + st * G_STAGE + (uint32_t)(G_TILE + k_off<64>(wm * 32 * WTM + l32, 2 * ks + hf));
     }
 
+  // The tile's 256 bias values go to LDS slice `buf` with its first k-tile
+  // (wave 0, two 256-byte copies; columns past N re-read the last one), so
+  // the epilogue reads them from LDS: a register load of the bias there
+  // would make the compiler wait for every vector memory operation in flight
+  // (the next tile's copies, the previous stores) before each use.
+  auto issue_bias = [&](int bn0, int buf) {
+    if (wave != 0) return;
+    const int last = (g.n - bn0 < GBN ? g.n - bn0 : GBN) * 2 - 4;  // byte offset of the last dword in range
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int o = 4 * lane + 256 * j;
+      lds_dma4((const char*)(g.bias + bn0), (uint32_t)(o < last ? o : last), base + G_BIAS + 512 * buf + 256 * j);
+    }
+  };
+
   int64_t m0;
   int n0;
   if (!tile_of(0, m0, n0)) return;
   Src cur;
   src_of(m0, n0, cur);
   issue(cur, 0, 0);
+  issue_bias(n0, 0);
   for (int64_t it = 0;; ++it) {
     f32x16 acc[WTN][WTM];
 #pragma unroll
@@ -217,6 +234,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
     if (more) {
       src_of(m0, n0, cur);
       issue(cur, 0, 0);
+      issue_bias(n0, (int)((it + 1) & 1));
     }
 
     // epilogue: element i of acc[ni][mi] is column n0 + 128 wn + 32 ni +
@@ -224,6 +242,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
     // (and GELU) and the bf16 rounding, the two lanes of a row (hf = 0, 1)
     // trade halves with permlane32 swaps so that each holds 8 consecutive
     // columns per store: hf 0 columns 8q..8q+7 for q = 0, 1; hf 1 for q = 2, 3.
+    const uint32_t bslice = base + G_BIAS + 512 * (uint32_t)(it & 1);  // this tile's bias in LDS
   #pragma unroll
     for (int mi = 0; mi < WTM; ++mi) {
       const int64_t m = tm0 + wm * 32 * WTM + mi * 32 + l32;
@@ -234,7 +253,8 @@ __global__ __launch_bounds__(kGThreads) void gemm_bt_kernel(GemmArgs g) {
         uint32_t d[4][2];
   #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const bf16x4 bb = *(const bf16x4*)(g.bias + nb + 8 * q + 4 * hf);
+          const bf16x4 bb =
+              *(lds_bf16x4*)(size_t)(bslice + (uint32_t)(wn * 128 + ni * 32 + 8 * q + 4 * hf) * 2);
           float v[4];
   #pragma unroll
           for (int j = 0; j < 4; ++j) {
