@@ -61,13 +61,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
-// i's bytes land at LDS byte lds_addr + 16 i.  base and lds_addr are
-// wave-uniform.  The copies are issued from inline assembly so that the
-// compiler does not track them: its own tracking would wait for every copy in
-// flight before the next LDS read of any buffer, which serialises the prefetch
-// with the compute.  The kernel waits for its copies itself (s_waitcnt
-// vmcnt) before the barrier that publishes a buffer.
+// Direct global->LDS copies (global_load_lds_dword / _dwordx4).  Base
+// pointers and LDS addresses are wave-uniform.  The copies are issued from
+// inline assembly so that the compiler does not track them: its own tracking
+// would wait for every copy in flight before the next LDS read of any buffer,
+// which serialises the prefetch with the compute.  The kernel waits for its
+// copies itself (s_waitcnt vmcnt) before the barrier that publishes a buffer.
+//
 // Every block rewrites its base SGPRs with a scalar self-copy (s_mov_b64 s,
 // s) before the loads: a VMEM instruction may read an SGPR only five wait
 // states after a VALU instruction wrote it (the base comes from
@@ -76,6 +76,7 @@ __device__ __forceinline__ float pair_sum(float x) {
 // and an SGPR last written by a scalar instruction needs none.  Without it
 // the load can take a stale base address.  The copy also gives the one wait
 // state a load needs after M0 is written.
+
 // A wave-uniform pointer as a 64-bit scalar value (readfirstlane returns
 // int: widen through uint32_t, never by sign extension).
 __device__ __forceinline__ uint64_t sbase(const char* p) {
@@ -84,7 +85,9 @@ __device__ __forceinline__ uint64_t sbase(const char* p) {
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(bv >> 32));
   return ((uint64_t)hi << 32) | lo;
 }
-// 16 bytes per lane (global_load_lds_dwordx4) from base + voff.
+
+// 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes, from base +
+// voff, land at LDS byte lds_addr + 16 i.
 __device__ __forceinline__ void lds_dma16(const char* base, uint32_t voff, uint32_t lds_addr) {
   uint64_t bs = sbase(base);
   uint32_t saved;
