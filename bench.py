@@ -114,25 +114,30 @@ def read_traffic():
         return None
 
 
-def probe_peak(dev, iters: int = 200000, reps: int = 2, random_operands: bool = False) -> float:
+def probe_peak(dev, iters: int = 200000, reps: int = 2, random_operands: bool = False, lds_reads: int = 0) -> float:
     """bf16 MFMA rate the part sustains under load (TFLOP/s): the library's
     MFMA-only probe on every CU (four 512-thread groups per CU, four waves per
     SIMD, ~50 ms per launch), best of `reps`.  Its operands are a fixed
     pattern of small values, or with `random_operands` seeded N(0, 1) bf16
-    values (more bits toggle per product: more power, a lower clock)."""
+    values (more bits toggle per product: more power, a lower clock).  With
+    `lds_reads` (4, 8 or 16; random operands) every product's first operand
+    comes from LDS, lds_reads / 16 KiB per product and wave, and `iters`
+    counts products / 4 as for the other forms."""
     import torch
     from long_context_exact_blockwise_amd import ringattn as ra
     wgs = 4 * 256
     out = torch.empty(wgs * ra.PROBE_THREADS, dtype=torch.float32, device=dev)
     ops = None
-    if random_operands:
+    if random_operands or lds_reads:
         g = torch.Generator(device=dev)
         g.manual_seed(0)
         ops = torch.randn(wgs * ra.PROBE_THREADS * ra.PROBE_OPERANDS_PER_THREAD, generator=g, device=dev,
                           dtype=torch.float32).to(torch.bfloat16)
 
     def launch(n):
-        if ops is None:
+        if lds_reads:
+            ra.ringattn_probe_mfma_lds(ops, out, wgs, max(1, n // 4), lds_reads)
+        elif ops is None:
             ra.ringattn_probe_mfma(out, wgs, n)
         else:
             ra.ringattn_probe_mfma_data(ops, out, wgs, n)
@@ -146,7 +151,10 @@ def probe_peak(dev, iters: int = 200000, reps: int = 2, random_operands: bool = 
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
-        f = wgs * (ra.PROBE_THREADS // 64) * iters * ra.PROBE_FLOP_PER_ITER_PER_WAVE
+        if lds_reads:
+            f = wgs * (ra.PROBE_THREADS // 64) * max(1, iters // 4) * ra.PROBE_LDS_FLOP_PER_ITER_PER_WAVE
+        else:
+            f = wgs * (ra.PROBE_THREADS // 64) * iters * ra.PROBE_FLOP_PER_ITER_PER_WAVE
         best = max(best, f / (ms * 1e-3) / 1e12)
     return best
 
@@ -582,6 +590,7 @@ def main():
 
     probed = probe_peak(dev) if wl.dtype == "bf16" else None
     probed_rand = probe_peak(dev, iters=100000, random_operands=True) if wl.dtype == "bf16" else None
+    probed_lds = probe_peak(dev, iters=100000, lds_reads=16) if wl.dtype == "bf16" else None
 
     if args.traffic_calib:
         n = 1 << 30
@@ -609,6 +618,12 @@ def main():
         "probed_peak_random_operands_note": "the same probe with seeded N(0, 1) bf16 operands "
                                             "(ringattn_probe_mfma_data): the rate the part sustains on data like "
                                             "the attention's, where power limits the clock",
+        "probed_peak_random_operands_lds_1k": probed_lds,
+        "frac_of_probed_random_operands_lds_1k": (achieved / probed_lds) if probed_lds else None,
+        "probed_peak_random_operands_lds_1k_note": "the random-operand probe with every product's first "
+                                                   "operand read from LDS, 1 KiB per product and wave "
+                                                   "(ringattn_probe_mfma_lds, lds_reads 16): the forward's "
+                                                   "ratio of LDS reads to products",
     }
     if wl.dtype != "bf16":
         roofline.update(bound="latency", peak=None, frac=None)

@@ -310,6 +310,21 @@ ra_status ringattn_probe_mfma(float* out, int32_t workgroups, int32_t iters, hip
 ra_status ringattn_probe_mfma_data(const void* operands, float* out, int32_t workgroups, int32_t iters,
                                    hipStream_t stream);
 
+/* Measurement helper, not part of the attention path: the probe with random
+ * operands (the layout of ringattn_probe_mfma_data) where every product's
+ * first operand is read from LDS.  Each workgroup copies its 32 KiB of
+ * operands twice into a 64 KiB LDS image; per iteration each wave reads
+ * `lds_reads` 16-byte-per-lane fragments (1 KiB each) from rotating windows
+ * of it and issues 16 products (16 * iters per wave in all), each fragment
+ * the first operand of 16 / lds_reads of them.  lds_reads = 16 moves 1 KiB of
+ * LDS per product and wave, the ratio of a kernel that reads both operands'
+ * tiles from LDS once per product (the forward's K and V^T fragments).  It
+ * gives the bf16 MFMA rate the part holds with that LDS traffic beside the
+ * matrix cores.  Errors: RA_E_NULL, RA_E_ALIGN, RA_E_SHAPE (workgroups in
+ * [1, 65536], iters in [1, 2^22], lds_reads not 4, 8 or 16), RA_E_MEMTYPE. */
+ra_status ringattn_probe_mfma_lds(const void* operands, float* out, int32_t workgroups, int32_t iters,
+                                  int32_t lds_reads, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

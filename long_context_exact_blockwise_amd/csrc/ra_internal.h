@@ -96,5 +96,7 @@ hipError_t launch_fill(float* p, int64_t n, hipStream_t s);  // n floats = +0.0f
 hipError_t launch_fill_u32(void* p, int64_t n, uint32_t value, hipStream_t s);  // n 32-bit words = value
 hipError_t launch_gemm_bt(const GemmArgs& g, hipStream_t s);
 hipError_t launch_probe_mfma(const void* src, float* out, int workgroups, int iters, hipStream_t s);
+hipError_t launch_probe_mfma_lds(const void* src, float* out, int workgroups, int iters, int lds_reads,
+                                 hipStream_t s);
 
 }  // namespace ra

@@ -776,4 +776,20 @@ ra_status ringattn_probe_mfma_data(const void* operands, float* out, int32_t wor
   return e == hipSuccess ? RA_OK : hip_fail(e, "probe launch");
 }
 
+ra_status ringattn_probe_mfma_lds(const void* operands, float* out, int32_t workgroups, int32_t iters,
+                                  int32_t lds_reads, hipStream_t stream) {
+  g_err.clear();
+  ra_status st;
+  if ((st = need_ptr(operands, "operands")) != RA_OK) return st;
+  if ((st = need_ptr(out, "out")) != RA_OK) return st;
+  if (workgroups < 1 || workgroups > 65536 || iters < 1 || iters > (1 << 22))
+    return fail(RA_E_SHAPE, "workgroups must be in [1, 65536] and iters in [1, 2^22]");
+  if (lds_reads != 4 && lds_reads != 8 && lds_reads != 16)
+    return fail(RA_E_SHAPE, "lds_reads must be 4, 8 or 16 (got %d)", lds_reads);
+  if ((st = check_mem(operands, false, "operands")) != RA_OK) return st;
+  if ((st = check_mem(out, false, "out")) != RA_OK) return st;
+  hipError_t e = ra::launch_probe_mfma_lds(operands, out, workgroups, iters, lds_reads, stream);
+  return e == hipSuccess ? RA_OK : hip_fail(e, "probe launch");
+}
+
 }  // extern "C"

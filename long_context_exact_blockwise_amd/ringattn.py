@@ -31,6 +31,7 @@ SYMBOLS = (
     "ringattn_block_class", "ringattn_init_state", "ringattn_block_fwd", "ringattn_finalize",
     "ringattn_ring_fwd", "ringattn_probe_copy", "ringattn_bwd_delta", "ringattn_block_bwd", "ringattn_ring_bwd",
     "ringattn_ffn_fwd", "ringattn_probe_mfma", "ringattn_ring_bwd_noalloc", "ringattn_probe_mfma_data",
+    "ringattn_probe_mfma_lds",
 )
 NOALLOC_MAX_ROWS = 4 << 20
 
@@ -107,6 +108,8 @@ def load(path: str):
     L.ringattn_probe_mfma.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P]
     L.ringattn_probe_mfma_data.restype = ctypes.c_int
     L.ringattn_probe_mfma_data.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, P]
+    L.ringattn_probe_mfma_lds.restype = ctypes.c_int
+    L.ringattn_probe_mfma_lds.argtypes = [P, P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P]
     L.ringattn_ffn_fwd.restype = ctypes.c_int
     L.ringattn_ffn_fwd.argtypes = [ctypes.POINTER(RaFfnDesc), P, P, P, P, P, P, P, P]
     L.ringattn_ring_bwd.restype = ctypes.c_int
@@ -236,6 +239,15 @@ PROBE_OPERANDS_PER_THREAD = 32  # bf16 values: four 8-element fragments
 
 def ringattn_probe_mfma_data(operands: torch.Tensor, out: torch.Tensor, workgroups: int, iters: int, stream=None):
     _check(lib().ringattn_probe_mfma_data(_ptr(operands), _ptr(out), workgroups, iters, _stream(stream)))
+
+
+PROBE_LDS_FLOP_PER_ITER_PER_WAVE = 16 * 32768  # sixteen 32x32x16 products
+
+
+def ringattn_probe_mfma_lds(operands: torch.Tensor, out: torch.Tensor, workgroups: int, iters: int, lds_reads: int,
+                            stream=None):
+    _check(lib().ringattn_probe_mfma_lds(_ptr(operands), _ptr(out), workgroups, iters, lds_reads,
+                                         _stream(stream)))
 
 
 # ---- convenience wrappers (allocation of outputs / workspace with torch) ----

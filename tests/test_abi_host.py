@@ -277,3 +277,14 @@ def test_probe_mfma_data_checks_before_enqueue():
     assert L.ringattn_probe_mfma_data(FAKE + 8, FAKE, 1, 1, None) == ra.RA_E_ALIGN
     assert L.ringattn_probe_mfma_data(FAKE, FAKE, 0, 1, None) == ra.RA_E_SHAPE
     assert L.ringattn_probe_mfma_data(FAKE, FAKE, 1, 1 << 25, None) == ra.RA_E_SHAPE
+
+
+def test_probe_mfma_lds_checks_before_enqueue():
+    L = ra.lib()
+    assert L.ringattn_probe_mfma_lds(None, FAKE, 1, 1, 16, None) == ra.RA_E_NULL
+    assert L.ringattn_probe_mfma_lds(FAKE, None, 1, 1, 16, None) == ra.RA_E_NULL
+    assert L.ringattn_probe_mfma_lds(FAKE + 8, FAKE, 1, 1, 16, None) == ra.RA_E_ALIGN
+    assert L.ringattn_probe_mfma_lds(FAKE, FAKE, 0, 1, 16, None) == ra.RA_E_SHAPE
+    assert L.ringattn_probe_mfma_lds(FAKE, FAKE, 1, 1 << 23, 16, None) == ra.RA_E_SHAPE
+    for bad in (0, 2, 12, 32, -16):
+        assert L.ringattn_probe_mfma_lds(FAKE, FAKE, 1, 1, bad, None) == ra.RA_E_SHAPE
