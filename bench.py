@@ -664,6 +664,10 @@ def main():
         if probed_rand:
             result["backward"]["pct_of_probed_peak_random_operands"] = (100.0 * result["backward"]["value"] /
                                                                         probed_rand)
+        if probed_lds:
+            # both backward kernels read about 1 KiB of LDS per product and wave, as the forward does
+            result["backward"]["pct_of_probed_peak_random_operands_lds_1k"] = (100.0 * result["backward"]["value"] /
+                                                                               probed_lds)
     if not args.no_ffn:
         result["ffn"] = ffn_measure(dev, 10, 2)
         if probed:
