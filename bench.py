@@ -56,6 +56,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SRC = [os.path.join(ROOT, "long_context_exact_blockwise_amd", "csrc", f)
               for f in ("attn_bf16.hip", "attn_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_fused_causal_q131072_p4_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_bf16_fused_causal_q131072_p4_stall_counters.txt")
 
 
 def visible_pairs(wl) -> int:
@@ -111,6 +112,28 @@ def read_traffic():
             return None
         return int(float(kv["hbm_bytes_per_launch"]))
     except (OSError, KeyError, ValueError):
+        return None
+
+
+def read_mfma_busy():
+    """Fraction of SIMD cycles the matrix cores were busy under the fused
+    kernel, from the committed rocprofv3 counter summary:
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).  None
+    when the file is missing or was taken on a different kernel source."""
+    try:
+        kv = {}
+        src = None
+        with open(COUNTERS_FILE) as f:
+            for line in f:
+                if line.startswith("kernel_source_sha256_16:"):
+                    src = line.split(":", 1)[1].strip()
+                parts = line.split()
+                if len(parts) == 2 and parts[0].isupper():
+                    kv[parts[0]] = float(parts[1])
+        if src != kernel_hash():
+            return None
+        return kv["SQ_VALU_MFMA_BUSY_CYCLES"] / (kv["GRBM_GUI_ACTIVE"] / 8 * 1024)
+    except (OSError, KeyError, ValueError, ZeroDivisionError):
         return None
 
 
@@ -606,6 +629,12 @@ def main():
     roofline = {
         "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+        "hbm_GBps": (traffic / (kern_ms * 1e-3) / 1e9) if traffic else None,
+        "hbm_GBps_note": "traffic (calibrated rocprofv3 FETCH_SIZE + WRITE_SIZE of the same kernel source) "
+                         "over this run's kernel time",
+        "mfma_busy": read_mfma_busy() if traffic else None,
+        "mfma_busy_note": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) "
+                          "from the committed counter summary of the same kernel source",
         "kernel": kname + (" (fused ring pass)" if not perblock else " (per block)"),
         "launches_per_step": 1 if (not perblock and len(kb) <= ra.RA_FUSED_MAX_BLOCKS) else None,
         "algorithmic_flop_per_step": f,

@@ -46,3 +46,12 @@ def test_backward_flops_are_five_products():
     wl = inputs.CONFIGS[3]
     assert bench.bwd_flops(wl) == 10 * 16 * 128 * 60_129_607_680
     assert bench.bwd_flops(wl) * 2 == bench.flops(wl) * 5
+
+
+def test_committed_counters_give_mfma_busy_and_traffic():
+    # the committed summaries match the current kernel source (else both are None)
+    busy = bench.read_mfma_busy()
+    traffic = bench.read_traffic()
+    assert busy is not None and traffic is not None
+    assert 0.3 < busy < 1.0
+    assert traffic > 5_377_097_728  # at least the algorithmic minimum (Q, K, V once; O, LSE once)
