@@ -26,7 +26,8 @@ namespace {
 
 // Eight waves, two per SIMD, of 64 rows x 128 columns.  (Four waves of
 // 128 x 128, one per SIMD, with half the LDS operand traffic per product,
-// measured 9-15% slower: nothing covers a wave's barrier and copy issue.)
+// measured 9-19% slower in several forms: with one wave per SIMD nothing
+// covers a wave's barrier, operand waits and epilogue.)
 constexpr int WTN = 4;                            // 32-column products per wave (128 columns)
 constexpr int WTM = 2;                            // 32-row products per wave (64 rows)
 constexpr int kGWaves = (256 / (32 * WTN)) * (256 / (32 * WTM));
