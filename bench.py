@@ -709,7 +709,7 @@ def main():
         torch.cuda.empty_cache()
         # (the host-streamed pass first: run after the 1M-token workload, its
         # host-to-device copies ran about 50% slower beside the kernels, 78
-        # against 57 ms per pass, on every box tried; alone, or after the
+        # against 57 ms per pass, on every board tried; alone, or after the
         # 32K-chunk workload, it takes the same 57 ms)
         ws_ = {name: workload_summary(dev, cfg) for name, cfg in
                (("chunk32k_p8_host_streamed", 5), ("chunk32k_p8", 2), ("tokens1m_p128", 4))}
