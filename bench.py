@@ -98,6 +98,28 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def source_hash(files, flags) -> str:
+    """Hash of kernel sources (names under the package's csrc/) and their
+    build flags, the tag each profile summary carries for the build it was
+    taken on."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "long_context_exact_blockwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    h.update(repr(flags).encode())
+    return h.hexdigest()[:16]
+
+
+def backward_hash() -> str:
+    from long_context_exact_blockwise_amd.build import SPLIT
+    return source_hash(("attn_bwd.hip", "attn_common.h"), SPLIT["attn_bwd.hip"])
+
+
+def feedforward_hash() -> str:
+    from long_context_exact_blockwise_amd.build import SOURCE_FLAGS
+    return source_hash(("ffn_bf16.hip", "attn_common.h"), SOURCE_FLAGS.get("ffn_bf16.hip", []))
+
+
 def read_traffic():
     """HBM bytes per launch from the committed counter summary, or None when
     missing or taken on a different kernel source."""

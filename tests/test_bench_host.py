@@ -55,3 +55,20 @@ def test_committed_counters_give_mfma_busy_and_traffic():
     assert busy is not None and traffic is not None
     assert 0.3 < busy < 1.0
     assert traffic > 5_377_097_728  # at least the algorithmic minimum (Q, K, V once; O, LSE once)
+
+
+def test_every_profile_summary_matches_the_current_sources():
+    # each summary under profiles/ names the hash of the kernel sources and
+    # flags it was taken on; a kernel change without new profiles fails here
+    want = {"kernel_source_sha256_16": bench.kernel_hash(),
+            "backward_source_and_flags_sha256_16": bench.backward_hash(),
+            "feedforward_source_and_flags_sha256_16": bench.feedforward_hash()}
+    prof = os.path.join(ROOT, "profiles")
+    seen = 0
+    for name in sorted(os.listdir(prof)):
+        for line in open(os.path.join(prof, name)):
+            key = line.split(":", 1)[0].strip()
+            if key in want:
+                assert line.split(":", 1)[1].strip() == want[key], (name, key)
+                seen += 1
+    assert seen >= 8
